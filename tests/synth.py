@@ -1,0 +1,150 @@
+"""Seeded synthetic inputs for RMSNorm training workloads.
+
+This module only draws random numbers and lays them out. It holds none of the
+method's arithmetic; the HIP path and the oracle both take their inputs from
+here.
+
+Recipe (the pages' workloads are synthetic: flashinfer PR "fix(cake_rmsnorm):
+sm_100a and sm_107a dw-accuracy backward routes", "Workload" paragraph):
+
+* generator: ``numpy.random.default_rng(seed)`` (PCG64);
+* activations x, r, dy, dres: ``standard_normal`` drawn in float32, rounded
+  to BF16 with round-to-nearest-even (torch's conversion);
+* weight: ``1 + 0.1 * standard_normal`` in float32, then rounded to the
+  weight dtype (BF16 or left in FP32);
+* heavy rows (large-T dw stress): ``round(0.01 * T)`` distinct rows chosen by
+  ``rng.choice(T, k, replace=False)`` have x scaled by 8 (exact in BF16);
+* per-head strided form: the whole ``[T, 8192]`` buffer is N(0,1); x is its
+  ``[:, :24*256]`` columns seen as ``[T, 24, 256]`` (row stride 8192, head
+  stride 256).
+
+Draw order within a workload is fixed: weight, x (or the strided buffer),
+heavy-row choice, r, dy, dres.
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Optional
+
+import numpy as np
+import torch
+
+EPS = 1e-6  # "Workload": eps 1e-6
+
+
+def bf16_bits(a32: np.ndarray) -> np.ndarray:
+    """float32 array -> BF16 bit patterns (uint16), nearest-even (torch)."""
+    t = torch.from_numpy(np.ascontiguousarray(a32, dtype=np.float32))
+    return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def bits_to_f32(bits: np.ndarray) -> np.ndarray:
+    """BF16 bit patterns -> float32 values (exact widening)."""
+    return (bits.astype(np.uint32) << 16).view(np.float32)
+
+
+def normal_bf16(rng: np.random.Generator, shape) -> np.ndarray:
+    return bf16_bits(rng.standard_normal(shape, dtype=np.float32))
+
+
+@dataclasses.dataclass
+class Weight:
+    dtype: str            # "bf16" or "f32"
+    bits: Optional[np.ndarray]   # uint16 patterns when dtype == "bf16"
+    f32: np.ndarray       # the weight's values as float32 (exact)
+
+    @property
+    def f64(self) -> np.ndarray:
+        return self.f32.astype(np.float64)
+
+    def raw(self) -> np.ndarray:
+        """The array handed to the library: uint16 bits or float32 values."""
+        return self.bits if self.dtype == "bf16" else self.f32
+
+
+def weight(rng: np.random.Generator, H: int, dtype: str) -> Weight:
+    w32 = (1.0 + 0.1 * rng.standard_normal(H, dtype=np.float32)).astype(np.float32)
+    if dtype == "bf16":
+        b = bf16_bits(w32)
+        return Weight("bf16", b, bits_to_f32(b))
+    if dtype == "f32":
+        return Weight("f32", None, w32)
+    raise ValueError(dtype)
+
+
+@dataclasses.dataclass
+class Workload:
+    """One seeded problem. Arrays are BF16 bit patterns unless noted.
+
+    ``x``/``dy``/``r``/``dres`` are logical ``[rows, H]`` arrays (rows = T*heads,
+    row = t*heads + head). For the strided per-head form, ``xbuf`` holds the
+    whole ``[T, row_stride]`` buffer and ``x`` is the gathered view.
+    """
+    name: str
+    T: int
+    heads: int
+    H: int
+    w: Weight
+    x: np.ndarray
+    dy: np.ndarray
+    r: Optional[np.ndarray] = None
+    dres: Optional[np.ndarray] = None
+    xbuf: Optional[np.ndarray] = None
+    x_stride_t: int = 0
+    x_stride_h: int = 0
+    heavy_rows: Optional[np.ndarray] = None
+    eps: float = EPS
+
+    @property
+    def rows(self) -> int:
+        return self.T * self.heads
+
+
+def make(T: int, H: int, w_dtype: str, seed: int, *, heads: int = 1,
+         residual: bool = False, with_dres: bool = True, heavy_frac: float = 0.0,
+         strided_row: int = 0, name: str = "") -> Workload:
+    """Build a workload. ``strided_row`` > 0 selects the strided per-head form:
+    x lives in a ``[T, strided_row]`` buffer with head stride H."""
+    rng = np.random.default_rng(seed)
+    w = weight(rng, H, w_dtype)
+    rows = T * heads
+    xbuf = None
+    st_t, st_h = heads * H, H
+    if strided_row:
+        assert strided_row >= heads * H
+        xbuf = normal_bf16(rng, (T, strided_row))
+        x = np.ascontiguousarray(xbuf[:, : heads * H]).reshape(rows, H)
+        st_t = strided_row
+    else:
+        x = normal_bf16(rng, (rows, H))
+    heavy = None
+    if heavy_frac > 0:
+        k = int(round(heavy_frac * T))
+        heavy = np.sort(rng.choice(T, k, replace=False))
+        xf = bits_to_f32(x)
+        xf[heavy] *= 8.0
+        x = bf16_bits(xf)
+    r = normal_bf16(rng, (rows, H)) if residual else None
+    dy = normal_bf16(rng, (rows, H))
+    dres = normal_bf16(rng, (rows, H)) if (residual and with_dres) else None
+    return Workload(name=name, T=T, heads=heads, H=H, w=w, x=x, dy=dy, r=r,
+                    dres=dres, xbuf=xbuf, x_stride_t=st_t, x_stride_h=st_h,
+                    heavy_rows=heavy)
+
+
+# The five workloads the method is quoted on (T, H, weight dtype, form).
+CONFIGS = {
+    "c1_T64_H256_f32w": dict(T=64, H=256, w_dtype="f32"),
+    "c2_T4096_H4096_bf16w": dict(T=4096, H=4096, w_dtype="bf16"),
+    "c3_T131072_H2048_f32w_heavy": dict(T=131072, H=2048, w_dtype="f32", heavy_frac=0.01),
+    "c4_res_T16384_H6144_bf16w": dict(T=16384, H=6144, w_dtype="bf16", residual=True),
+    "c5a_heads_T32768x24x256_strided8192_f32w": dict(T=32768, heads=24, H=256, w_dtype="f32",
+                                                     strided_row=8192),
+    "c5b_heads_T32768x4x256_f32w": dict(T=32768, heads=4, H=256, w_dtype="f32"),
+}
+
+
+def config(name: str, seed: int = 0, **overrides) -> Workload:
+    kw = dict(CONFIGS[name])
+    kw.update(overrides)
+    return make(seed=seed, name=name, **kw)
