@@ -1,0 +1,238 @@
+"""RMSNorm for training on MI355X (gfx950): Python face of the C ABI.
+
+The functions below carry the C ABI's names (include/rmsnorm.h) and only
+marshal torch tensors into pointers, views and the current HIP stream; the
+work is done by the HIP kernels in ``libbwd_rmsnorm.so``. Tensors must live
+on a ROCm device. Outputs not supplied are allocated with torch.
+
+Tensor conventions: x/dy/y/dx/h/r/dres are ``torch.bfloat16`` tensors of
+shape [T, H] (plain) or [T, heads, H] (per-head view; any strides whose last
+one is 1); w is bfloat16 or float32 of shape [H]; rstd is float32 of
+[T] / [T, heads]; dw is float32 [H].
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Optional, Tuple
+
+import torch
+
+from . import _lib
+from ._lib import RMSNormError, View  # noqa: F401
+
+__all__ = [
+    "rmsnorm_fwd", "rmsnorm_fwd_strided", "rmsnorm_residual_fwd", "rmsnorm_bwd",
+    "rmsnorm_bwd_strided", "rmsnorm_residual_bwd", "rmsnorm_bwd_workspace_bytes",
+    "rmsnorm_workspace_init", "rmsnorm_status_string", "rmsnorm_route_query",
+    "rmsnorm_timing_enable", "rmsnorm_timing_read", "RMSNormError", "View",
+]
+
+
+def _stream(dev: torch.device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[ctypes.c_void_p]:
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _wdtype(w: torch.Tensor) -> int:
+    if w.dtype == torch.bfloat16:
+        return _lib.RMSN_BF16
+    if w.dtype == torch.float32:
+        return _lib.RMSN_F32
+    raise TypeError(f"weight dtype must be bfloat16 or float32, got {w.dtype}")
+
+
+def _need_bf16(name: str, t: torch.Tensor) -> None:
+    if t.dtype != torch.bfloat16:
+        raise TypeError(f"{name} must be bfloat16, got {t.dtype}")
+    if not t.is_cuda:
+        raise TypeError(f"{name} must be a device tensor")
+
+
+def _view(t: torch.Tensor) -> View:
+    """[T, H] or [T, heads, H] tensor -> C view (element strides)."""
+    if t.dim() == 2:
+        T, H = t.shape
+        if t.stride(1) != 1:
+            raise ValueError("the last dimension must be contiguous")
+        return View(T, 1, H, t.stride(0), 0)
+    if t.dim() == 3:
+        T, heads, H = t.shape
+        if t.stride(2) != 1:
+            raise ValueError("the last dimension must be contiguous")
+        return View(T, heads, H, t.stride(0), t.stride(1))
+    raise ValueError("expected a [T, H] or [T, heads, H] tensor")
+
+
+def _contig2d(name: str, t: torch.Tensor) -> Tuple[int, int]:
+    if t.dim() != 2 or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous [T, H] tensor")
+    return t.shape[0], t.shape[1]
+
+
+# ------------------------------------------------------------------ forward
+
+def rmsnorm_fwd(x: torch.Tensor, w: torch.Tensor, eps: float = 1e-6,
+                y: Optional[torch.Tensor] = None, rstd: Optional[torch.Tensor] = None):
+    """y, rstd = RMSNorm forward of contiguous x[T, H]."""
+    _need_bf16("x", x)
+    T, H = _contig2d("x", x)
+    y = torch.empty_like(x) if y is None else y
+    rstd = torch.empty(T, dtype=torch.float32, device=x.device) if rstd is None else rstd
+    _lib.check(_lib.load().rmsnorm_fwd(_ptr(x), _ptr(w), _wdtype(w), float(eps), _ptr(y),
+                                       _ptr(rstd), T, H, _stream(x.device)))
+    return y, rstd
+
+
+def rmsnorm_fwd_strided(x: torch.Tensor, w: torch.Tensor, eps: float = 1e-6,
+                        y: Optional[torch.Tensor] = None, rstd: Optional[torch.Tensor] = None):
+    """Forward over a [T, heads, H] (or [T, H]) view with arbitrary row strides."""
+    _need_bf16("x", x)
+    xv = _view(x)
+    if y is None:
+        y = torch.empty(x.shape, dtype=torch.bfloat16, device=x.device)
+    if rstd is None:
+        rstd = torch.empty(x.shape[:-1], dtype=torch.float32, device=x.device)
+    _lib.check(_lib.load().rmsnorm_fwd_strided(_ptr(x), xv, _ptr(w), _wdtype(w), float(eps),
+                                               _ptr(y), _view(y), _ptr(rstd), _stream(x.device)))
+    return y, rstd
+
+
+def rmsnorm_residual_fwd(x: torch.Tensor, r: torch.Tensor, w: torch.Tensor, eps: float = 1e-6,
+                         h: Optional[torch.Tensor] = None, y: Optional[torch.Tensor] = None,
+                         rstd: Optional[torch.Tensor] = None):
+    """h = BF16(x + r); y, rstd = RMSNorm(h). Returns (h, y, rstd)."""
+    _need_bf16("x", x)
+    _need_bf16("r", r)
+    T, H = _contig2d("x", x)
+    h = torch.empty_like(x) if h is None else h
+    y = torch.empty_like(x) if y is None else y
+    rstd = torch.empty(T, dtype=torch.float32, device=x.device) if rstd is None else rstd
+    _lib.check(_lib.load().rmsnorm_residual_fwd(_ptr(x), _ptr(r), _ptr(w), _wdtype(w), float(eps),
+                                                _ptr(h), _ptr(y), _ptr(rstd), T, H,
+                                                _stream(x.device)))
+    return h, y, rstd
+
+
+# ----------------------------------------------------------------- backward
+
+_WS_CACHE = {}
+
+
+def rmsnorm_bwd_workspace_bytes(rows: int, H: int, w_dtype: torch.dtype, deterministic: bool) -> int:
+    wd = _lib.RMSN_BF16 if w_dtype == torch.bfloat16 else _lib.RMSN_F32
+    return int(_lib.load().rmsnorm_bwd_workspace_bytes(rows, H, wd, int(bool(deterministic))))
+
+
+def rmsnorm_workspace_init(ws: torch.Tensor) -> None:
+    _lib.check(_lib.load().rmsnorm_workspace_init(_ptr(ws), ws.numel() * ws.element_size(),
+                                                  _stream(ws.device)))
+
+
+def _workspace(dev: torch.device, nbytes: int, deterministic: bool) -> Optional[torch.Tensor]:
+    """Per (device, stream) workspace. The non-deterministic kernels need it
+    zero-filled on first use and leave it zero-filled."""
+    if nbytes == 0:
+        return None
+    key = (dev, torch.cuda.current_stream(dev).cuda_stream, bool(deterministic))
+    ws = _WS_CACHE.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.empty(max(nbytes, 1 << 20) + 256, dtype=torch.uint8, device=dev)
+        off = (-ws.data_ptr()) % 256
+        ws = ws[off:]
+        if not deterministic:
+            rmsnorm_workspace_init(ws)
+        _WS_CACHE[key] = ws
+    return ws
+
+
+def rmsnorm_bwd(dy: torch.Tensor, x: torch.Tensor, rstd: torch.Tensor, w: torch.Tensor,
+                deterministic: bool = True, dx: Optional[torch.Tensor] = None,
+                dw: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None):
+    """dx, dw of RMSNorm for contiguous [T, H] tensors."""
+    _need_bf16("dy", dy)
+    _need_bf16("x", x)
+    T, H = _contig2d("x", x)
+    dx = torch.empty_like(x) if dx is None else dx
+    dw = torch.empty(H, dtype=torch.float32, device=x.device) if dw is None else dw
+    need = rmsnorm_bwd_workspace_bytes(T, H, w.dtype, deterministic)
+    ws = workspace if workspace is not None else _workspace(x.device, need, deterministic)
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _lib.check(_lib.load().rmsnorm_bwd(_ptr(dy), _ptr(x), _ptr(rstd), _ptr(w), _wdtype(w),
+                                       int(bool(deterministic)), _ptr(dx), _ptr(dw), T, H,
+                                       _ptr(ws), nbytes, _stream(x.device)))
+    return dx, dw
+
+
+def rmsnorm_bwd_strided(dy: torch.Tensor, x: torch.Tensor, rstd: torch.Tensor, w: torch.Tensor,
+                        deterministic: bool = True, dx: Optional[torch.Tensor] = None,
+                        dw: Optional[torch.Tensor] = None,
+                        workspace: Optional[torch.Tensor] = None):
+    """Backward over [T, heads, H] views; dw sums over T and heads."""
+    _need_bf16("dy", dy)
+    _need_bf16("x", x)
+    xv = _view(x)
+    rows = xv.T * xv.heads
+    if dx is None:
+        dx = torch.empty(x.shape, dtype=torch.bfloat16, device=x.device)
+    dw = torch.empty(xv.H, dtype=torch.float32, device=x.device) if dw is None else dw
+    need = rmsnorm_bwd_workspace_bytes(rows, xv.H, w.dtype, deterministic)
+    ws = workspace if workspace is not None else _workspace(x.device, need, deterministic)
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _lib.check(_lib.load().rmsnorm_bwd_strided(_ptr(dy), _view(dy), _ptr(x), xv, _ptr(rstd),
+                                               _ptr(w), _wdtype(w), int(bool(deterministic)),
+                                               _ptr(dx), _view(dx), _ptr(dw), _ptr(ws), nbytes,
+                                               _stream(x.device)))
+    return dx, dw
+
+
+def rmsnorm_residual_bwd(dy: torch.Tensor, h: torch.Tensor, rstd: torch.Tensor, w: torch.Tensor,
+                         dres: Optional[torch.Tensor] = None, deterministic: bool = True,
+                         dh: Optional[torch.Tensor] = None, dw: Optional[torch.Tensor] = None,
+                         workspace: Optional[torch.Tensor] = None):
+    """dh (the combined gradient for x and r) and dw of the residual form."""
+    _need_bf16("dy", dy)
+    _need_bf16("h", h)
+    T, H = _contig2d("h", h)
+    dh = torch.empty_like(h) if dh is None else dh
+    dw = torch.empty(H, dtype=torch.float32, device=h.device) if dw is None else dw
+    need = rmsnorm_bwd_workspace_bytes(T, H, w.dtype, deterministic)
+    ws = workspace if workspace is not None else _workspace(h.device, need, deterministic)
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _lib.check(_lib.load().rmsnorm_residual_bwd(_ptr(dy), _ptr(h), _ptr(dres), _ptr(rstd), _ptr(w),
+                                                _wdtype(w), int(bool(deterministic)), _ptr(dh),
+                                                _ptr(dw), T, H, _ptr(ws), nbytes,
+                                                _stream(h.device)))
+    return dh, dw
+
+
+# -------------------------------------------------------------- diagnostics
+
+def rmsnorm_status_string(status: int) -> str:
+    return _lib.status_string(status)
+
+
+def rmsnorm_route_query(op: str, rows: int, H: int, w_dtype: torch.dtype = torch.bfloat16,
+                        deterministic: bool = True, residual: bool = False) -> dict:
+    """Route-table entry for op 'fwd' or 'bwd' (host only, no GPU needed)."""
+    info = _lib.RouteInfo()
+    wd = _lib.RMSN_BF16 if w_dtype == torch.bfloat16 else _lib.RMSN_F32
+    _lib.check(_lib.load().rmsnorm_route_query(0 if op == "fwd" else 1, rows, H, wd,
+                                               int(bool(deterministic)), int(bool(residual)),
+                                               ctypes.byref(info)))
+    return info.as_dict()
+
+
+def rmsnorm_timing_enable(enable: bool = True) -> None:
+    _lib.check(_lib.load().rmsnorm_timing_enable(int(bool(enable))))
+
+
+def rmsnorm_timing_read() -> dict:
+    """{timer index: (launches, total_ms)} accumulated since the last read."""
+    n = _lib.RMSN_TIMER_COUNT
+    launches = (ctypes.c_int64 * n)()
+    ms = (ctypes.c_double * n)()
+    _lib.check(_lib.load().rmsnorm_timing_read(launches, ms, n))
+    return {i: (int(launches[i]), float(ms[i])) for i in range(n)}

@@ -1,0 +1,104 @@
+// Device-side helpers for the gfx950 RMSNorm kernels: BF16 pack/unpack,
+// 16-byte vector access, row addressing and lane-group reductions.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "rmsn_internal.h"
+
+namespace rmsn {
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// BF16 -> FP32 is exact: the 16 bits are the top half of the FP32 pattern.
+__device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
+
+// Two FP32 -> two BF16, round to nearest even (one v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+    f32x2 v = {a, b};
+    bf16x2 r = __builtin_convertvector(v, bf16x2);
+    return __builtin_bit_cast(uint32_t, r);
+}
+
+__device__ __forceinline__ void unpack8(const uint4& v, float (&f)[8]) {
+    f[0] = bf16_lo(v.x); f[1] = bf16_hi(v.x);
+    f[2] = bf16_lo(v.y); f[3] = bf16_hi(v.y);
+    f[4] = bf16_lo(v.z); f[5] = bf16_hi(v.z);
+    f[6] = bf16_lo(v.w); f[7] = bf16_hi(v.w);
+}
+
+__device__ __forceinline__ uint4 pack8(const float (&f)[8]) {
+    uint4 v;
+    v.x = pack_bf16x2(f[0], f[1]);
+    v.y = pack_bf16x2(f[2], f[3]);
+    v.z = pack_bf16x2(f[4], f[5]);
+    v.w = pack_bf16x2(f[6], f[7]);
+    return v;
+}
+
+__device__ __forceinline__ uint4 ld16(const uint16_t* p) {
+    return *reinterpret_cast<const uint4*>(p);
+}
+__device__ __forceinline__ void st16(uint16_t* p, const uint4& v) {
+    *reinterpret_cast<uint4*>(p) = v;
+}
+
+// Weight vector of 8 elements as FP32 (BF16 widened exactly).
+template <typename WT>
+__device__ __forceinline__ void load_w8(const void* w, int v, float (&f)[8]);
+
+template <>
+__device__ __forceinline__ void load_w8<uint16_t>(const void* w, int v, float (&f)[8]) {
+    uint4 q = ld16(static_cast<const uint16_t*>(w) + (int64_t)v * kVec);
+    unpack8(q, f);
+}
+
+template <>
+__device__ __forceinline__ void load_w8<float>(const void* w, int v, float (&f)[8]) {
+    const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(w) + (int64_t)v * kVec);
+    float4 a = p[0], b = p[1];
+    f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w;
+    f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
+}
+
+// Element offset of row r = (t, head) under an addressing rule.
+__device__ __forceinline__ int64_t row_offset(int64_t r, int32_t heads, const RowAddr& a) {
+    if (heads == 1) return r * a.st_t;
+    // rows fit in 32 bits for every supported shape (checked on the host)
+    uint32_t ur = (uint32_t)r, uh = (uint32_t)heads;
+    uint32_t t = ur / uh;
+    uint32_t hd = ur - t * uh;
+    return (int64_t)t * a.st_t + (int64_t)hd * a.st_h;
+}
+
+// Butterfly sum over aligned groups of G lanes (G a power of two <= 64);
+// every lane of the group receives the group's sum. The pairing order is
+// fixed, so the result is bit-reproducible.
+template <int G>
+__device__ __forceinline__ float group_sum(float v) {
+#pragma unroll
+    for (int m = G / 2; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
+    return v;
+}
+
+template <int G>
+__device__ __forceinline__ double group_sum(double v) {
+#pragma unroll
+    for (int m = G / 2; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
+    return v;
+}
+
+// Runtime-width variant (g a power of two <= 64).
+__device__ __forceinline__ float group_sum_rt(float v, int g) {
+    for (int m = g >> 1; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
+    return v;
+}
+__device__ __forceinline__ double group_sum_rt(double v, int g) {
+    for (int m = g >> 1; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
+    return v;
+}
+
+}  // namespace rmsn

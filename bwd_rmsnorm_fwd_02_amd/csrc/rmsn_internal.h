@@ -1,0 +1,89 @@
+// Internal declarations shared by the C-ABI layer and the kernel launchers.
+// Host-visible only: parameter blocks passed by value to the kernels, and
+// the launcher entry points each kernel file provides.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/rmsnorm.h"
+
+namespace rmsn {
+
+// Widths the kernels are compiled for: vectors of 8 BF16 (16 bytes) per lane.
+constexpr int kVec = 8;
+constexpr int64_t kMaxH = 16384;
+// The partition of rows into dw partials is derived from this fixed CU count,
+// never from the device, so deterministic dw bits do not depend on the part.
+constexpr int kPartitionCUs = 256;
+
+// Addressing of one tensor: row r = (t, head) starts at t*st_t + head*st_h.
+struct RowAddr {
+    int64_t st_t;
+    int64_t st_h;
+};
+
+struct FwdParams {
+    const uint16_t* x;
+    const uint16_t* r;      // residual input (residual form) or null
+    uint16_t* h;            // residual output h = BF16(x + r) or null
+    uint16_t* y;
+    float* rstd;
+    const void* w;
+    RowAddr ax, ar, ah, ay;
+    int64_t rows;
+    int32_t heads;
+    int32_t H;
+    int32_t nvec;           // H / 8
+    int32_t tpr;            // lanes per row
+    int32_t rpb;            // row slots per block
+    float eps;
+};
+
+struct BwdParams {
+    const uint16_t* dy;
+    const uint16_t* x;      // x, or h in the residual form
+    const uint16_t* dres;   // residual-stream gradient or null
+    const float* rstd;
+    const void* w;
+    uint16_t* dx;
+    float* dw;              // written by the finalising kernel/block
+    void* partial;          // [P, H] FP32 or FP64 partials (deterministic route)
+    double* acc;            // [H] FP64 accumulator (atomic route)
+    unsigned int* ticket;   // block counter (atomic route)
+    RowAddr ady, ax, ares, adx;
+    int64_t rows;
+    int32_t heads;
+    int32_t H;
+    int32_t nvec;
+    int32_t tpr;
+    int32_t rpb;
+    int32_t ncol_blocks;    // column-task blocks (small-T kernel)
+    int32_t col_splits;     // row splits per column task (small-T kernel)
+};
+
+struct Route {
+    rmsn_route_t r;
+    size_t workspace;       // bytes needed
+};
+
+// Route table (route.cpp). op 0 fwd, 1 bwd.
+int route(int op, int64_t rows, int64_t H, rmsn_dtype_t wdt, int det, int residual,
+          Route* out);
+
+// Launchers (one per kernel file). They launch on `s` and return
+// hipGetLastError() mapped to an RMSN status.
+int launch_fwd(const FwdParams& p, const Route& rt, rmsn_dtype_t wdt, bool residual,
+               hipStream_t s);
+int launch_bwd_row(const BwdParams& p, const Route& rt, rmsn_dtype_t wdt, bool residual,
+                   hipStream_t s);
+int launch_dw_reduce(const BwdParams& p, const Route& rt, hipStream_t s);
+int launch_bwd_small(const BwdParams& p, const Route& rt, rmsn_dtype_t wdt, bool residual,
+                     hipStream_t s);
+int launch_fill_zero(void* ptr, size_t bytes, hipStream_t s);
+
+// Kernel timing hooks (api.cpp): bracket a launch when timing is enabled.
+void timer_begin(int kind, hipStream_t s);
+void timer_end(int kind, hipStream_t s);
+
+}  // namespace rmsn

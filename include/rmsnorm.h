@@ -1,0 +1,194 @@
+/*
+ * rmsnorm.h — C ABI of the MI355X (gfx950) RMSNorm-for-training library.
+ *
+ * The operation (flashinfer PR "fix(cake_rmsnorm): sm_100a and sm_107a
+ * dw-accuracy backward routes", opening description):
+ *   forward   x[T, H] BF16, w[H] BF16 or FP32  ->  y[T, H] BF16, rstd[T] FP32
+ *             rstd_t = 1/sqrt(mean_j(x_tj^2) + eps),  y_tj = x_tj * rstd_t * w_j
+ *   backward  dy[T, H] BF16                     ->  dx[T, H] BF16, dw[H] FP32
+ *             xhat = x*rstd, c_t = mean_j(dy_tj * w_j * xhat_tj),
+ *             dx_tj = rstd_t * (dy_tj * w_j - xhat_tj * c_t),
+ *             dw_j = sum_t dy_tj * xhat_tj
+ * The two backward modes (deterministic = 1 or 0) share the forward and
+ * differ only in how the dw column sum over T is reduced. Forms (same page):
+ * plain [T, H] rows with BF16 or FP32 weight; a fused residual add
+ * (h_new = BF16(h + u), "Key" paragraph); per-head views [T, heads, H]
+ * (strided or contiguous) that share one w[H], with dw summed over T and
+ * heads. Workload conventions ("Workload" paragraph): y, dx and h_new BF16;
+ * rstd and dw FP32.
+ *
+ * Conventions for every entry point:
+ * - All tensor pointers are DEVICE pointers on the current HIP device; the
+ *   caller owns every buffer. The library never allocates, frees or
+ *   synchronises; each call enqueues kernels on `stream` and returns.
+ * - BF16 tensors are raw 16-bit patterns (void*). Sizes and strides are in
+ *   ELEMENTS (int64_t).
+ * - A view describes rows = T * heads rows of H contiguous elements; row
+ *   (t, head) starts at t * stride_t + head * stride_h. rstd is always a
+ *   contiguous FP32 array of T * heads values, index t * heads + head.
+ * - Requirements: H a positive multiple of 8 and at most 16384; T, heads >= 0
+ *   (rows == 0 is a no-op that returns RMSN_OK); BF16 tensor base pointers
+ *   and strides 16-byte aligned (strides multiples of 8 elements); FP32
+ *   weight/rstd/dw pointers 4-byte aligned; eps finite and >= 0.
+ * - Outputs are written in full (dw is overwritten, never accumulated into).
+ *   An output may alias an input only exactly (same pointer, same view), for
+ *   y/x in the forward and dx/dy in the backward; any other overlap of the
+ *   byte spans of an output with another tensor is RMSN_ERR_ALIAS.
+ * - Errors are returned as negative status codes before anything is
+ *   enqueued (RMSN_ERR_LAUNCH is reported after a failed launch).
+ *   rmsnorm_status_string() names them. Nothing is printed.
+ * - Workspace: rmsnorm_bwd and rmsnorm_residual_bwd take a device workspace
+ *   of at least rmsnorm_bwd_workspace_bytes(...) bytes, 256-byte aligned.
+ *   For deterministic == 0 the workspace must be zero-filled before its
+ *   first use (rmsnorm_workspace_init, or any zero fill); every completed
+ *   non-deterministic call leaves it zero-filled again. Two calls that may
+ *   run concurrently must not share a workspace.
+ */
+#ifndef RMSNORM_MI355X_H
+#define RMSNORM_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { RMSN_BF16 = 0, RMSN_F32 = 1 } rmsn_dtype_t;
+
+enum {
+    RMSN_OK = 0,
+    RMSN_ERR_NULL = -1,      /* a required pointer is NULL */
+    RMSN_ERR_DTYPE = -2,     /* weight dtype is neither RMSN_BF16 nor RMSN_F32 */
+    RMSN_ERR_SHAPE = -3,     /* H not in 8..16384 step 8, negative T/heads, views disagree */
+    RMSN_ERR_ALIGN = -4,     /* pointer or stride misaligned */
+    RMSN_ERR_WORKSPACE = -5, /* workspace NULL, misaligned or smaller than required */
+    RMSN_ERR_OVERFLOW = -6,  /* element offsets or byte sizes overflow int64 */
+    RMSN_ERR_ALIAS = -7,     /* an output overlaps another tensor (not exact in-place) */
+    RMSN_ERR_LAUNCH = -8,    /* a kernel launch failed (hipGetLastError) */
+    RMSN_ERR_EPS = -9        /* eps negative, NaN or infinite */
+};
+
+typedef struct {
+    int64_t T;        /* tokens */
+    int64_t heads;    /* rows per token (1 for plain [T, H]) */
+    int64_t H;        /* normalised width */
+    int64_t stride_t; /* elements between tokens */
+    int64_t stride_h; /* elements between heads of one token */
+} rmsn_view_t;
+
+/* ---------------------------------------------------------------- forward */
+
+/* Plain forward over contiguous x[T, H] -> y[T, H], rstd[T].
+ * (flashinfer PR #8827 description: forward returns y BF16, rstd FP32.) */
+int rmsnorm_fwd(const void* x, const void* w, rmsn_dtype_t w_dtype, float eps,
+                void* y, float* rstd, int64_t T, int64_t H, hipStream_t stream);
+
+/* Forward over arbitrary views (per-head [T, heads, H], strided or not).
+ * x and y views must agree on T, heads and H; rstd has T*heads entries.
+ * (Same page: per-head views [T,24,256] strided and [T,4,256] contiguous
+ * with a shared w[256].) */
+int rmsnorm_fwd_strided(const void* x, rmsn_view_t xv, const void* w,
+                        rmsn_dtype_t w_dtype, float eps, void* y, rmsn_view_t yv,
+                        float* rstd, hipStream_t stream);
+
+/* Fused residual forward on contiguous [T, H]: h = BF16(x + r) is written,
+ * then y, rstd = RMSNorm(h). (Same page, "Key": h_new = BF16(h + u).) */
+int rmsnorm_residual_fwd(const void* x, const void* r, const void* w,
+                         rmsn_dtype_t w_dtype, float eps, void* h, void* y,
+                         float* rstd, int64_t T, int64_t H, hipStream_t stream);
+
+/* --------------------------------------------------------------- backward */
+
+/* Bytes of workspace the backward needs for this shape and mode (0 when the
+ * chosen kernels need none; callers may still pass a larger buffer). */
+size_t rmsnorm_bwd_workspace_bytes(int64_t rows, int64_t H, rmsn_dtype_t w_dtype,
+                                   int deterministic);
+
+/* Zero-fill a workspace with a kernel on `stream` (safe inside graph capture). */
+int rmsnorm_workspace_init(void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Plain backward on contiguous [T, H]. rstd is the forward's FP32 output.
+ * deterministic != 0: dw is bit-identical run to run for the same inputs and
+ * does not depend on the device's CU count; deterministic == 0 may reduce dw
+ * with atomics. dx is bit-identical between the two modes.
+ * (Same page: deterministic=True and =False share the forward and differ
+ * only in the backward; dw budget "per element atol 1e-4 + rtol 1e-4 vs
+ * FP64" in "Changed windows by reason".) */
+int rmsnorm_bwd(const void* dy, const void* x, const float* rstd, const void* w,
+                rmsn_dtype_t w_dtype, int deterministic, void* dx, float* dw,
+                int64_t T, int64_t H, void* workspace, size_t workspace_bytes,
+                hipStream_t stream);
+
+/* Backward over views: dy, x and dx views agree on T, heads and H; dw[H]
+ * sums over T and heads. */
+int rmsnorm_bwd_strided(const void* dy, rmsn_view_t dyv, const void* x, rmsn_view_t xv,
+                        const float* rstd, const void* w, rmsn_dtype_t w_dtype,
+                        int deterministic, void* dx, rmsn_view_t dxv, float* dw,
+                        void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Residual backward on contiguous [T, H]: h is the forward's BF16 h_new;
+ * dres (nullable) is the gradient arriving at h_new from the residual
+ * stream. Returns dh = BF16(dres + dRMSNorm/dh) — the one "combined grad"
+ * that flows to both x and r — and dw. (Same page, "Key": fused residual
+ * add, combined grad.) */
+int rmsnorm_residual_bwd(const void* dy, const void* h, const void* dres,
+                         const float* rstd, const void* w, rmsn_dtype_t w_dtype,
+                         int deterministic, void* dh, float* dw, int64_t T, int64_t H,
+                         void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------ diagnostics */
+
+/* Static description of an error code (never NULL). */
+const char* rmsnorm_status_string(int status);
+
+/* Kernel kinds a route can name. */
+enum {
+    RMSN_KIND_FWD_ROW = 1,      /* one-pass row forward */
+    RMSN_KIND_BWD_ROW_DET = 2,  /* row backward + per-block dw partials, then fixed-order reduce */
+    RMSN_KIND_BWD_ROW_ATOMIC = 3, /* row backward + FP64 atomic dw, last block finalises */
+    RMSN_KIND_BWD_COLTASK = 4   /* small T: fixed column tasks for dw + row tasks for dx */
+};
+
+typedef struct {
+    int kind;            /* RMSN_KIND_* */
+    int vec_per_lane;    /* 16-byte vectors each lane owns per row */
+    int lanes_per_row;   /* threads that share one row */
+    int rows_per_block;  /* rows a block works on at once */
+    int block_threads;
+    int partial_f64;     /* dw partials in FP64 (1) or FP32 (0) */
+    int64_t grid;        /* blocks of the main kernel */
+    int64_t partials;    /* dw partial rows written (0 if none) */
+    int64_t reduce_grid; /* blocks of the dw reduce kernel (0 if none) */
+} rmsn_route_t;
+
+/* The route table: which kernel and launch shape serve this problem.
+ * op: 0 forward, 1 backward. Pure host function; needs no GPU.
+ * Returns RMSN_OK or RMSN_ERR_SHAPE / RMSN_ERR_DTYPE / RMSN_ERR_NULL. */
+int rmsnorm_route_query(int op, int64_t rows, int64_t H, rmsn_dtype_t w_dtype,
+                        int deterministic, int residual, rmsn_route_t* out);
+
+/* Per-kernel timing with HIP events on the caller's stream (for benchmarks).
+ * While enabled, every kernel the library launches is bracketed by two
+ * events; rmsnorm_timing_read waits for them and returns, per kernel kind
+ * (index 0..7, see RMSN_TIMER_*), the number of launches and their summed
+ * duration in milliseconds, then clears the counters. Not thread-safe;
+ * off by default. */
+enum {
+    RMSN_TIMER_FWD = 0,
+    RMSN_TIMER_BWD_ROW = 1,
+    RMSN_TIMER_DW_REDUCE = 2,
+    RMSN_TIMER_BWD_SMALL = 3,
+    RMSN_TIMER_INIT = 4,
+    RMSN_TIMER_COUNT = 8
+};
+int rmsnorm_timing_enable(int enable);
+int rmsnorm_timing_read(int64_t* launches, double* total_ms, int n);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RMSNORM_MI355X_H */

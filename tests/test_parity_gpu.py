@@ -1,0 +1,319 @@
+"""Parity of the HIP path (through the C ABI) with the FP64 oracle.
+
+Small shapes span several blocks, ragged rows (H not a multiple of the lane
+count), both weight dtypes, both modes, the small-T column-task route and
+the large-T row route. Full-size cases run each workload the method is
+quoted on, in the same launch configuration the benchmark times, and check
+sampled rows of y/dx element by element, every row's rstd, every column of
+dw, and bit-reproducibility of deterministic dw.
+
+The backward is fed the oracle's rstd rounded to FP32 (never the GPU
+forward's), so no oracle input comes from the HIP path.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import bwd_rmsnorm_fwd_02_amd as rn
+import oracle
+from tests import synth
+from tests.parity import (check_bf16_strict, check_dw, check_dx, check_rstd, dx_bound,
+                          oracle_rstd32, to_f64)
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def dev_bf16(bits: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(DEV)
+
+
+def host_bits(t: torch.Tensor) -> np.ndarray:
+    return t.detach().contiguous().cpu().view(torch.int16).numpy().view(np.uint16)
+
+
+def dev_w(w: synth.Weight) -> torch.Tensor:
+    if w.dtype == "bf16":
+        return dev_bf16(w.bits)
+    return torch.from_numpy(w.f32.copy()).to(DEV)
+
+
+def dev_f32(a: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(DEV)
+
+
+def _announce(msg: str) -> None:
+    print(msg, flush=True)
+
+
+# ------------------------------------------------------------ small shapes
+
+SMALL = [
+    (1, 8, "f32"), (3, 24, "bf16"), (64, 256, "f32"), (65, 256, "f32"), (37, 4096, "bf16"),
+    (300, 2048, "f32"), (129, 6144, "bf16"), (70, 1032, "bf16"), (257, 16384, "bf16"),
+    (1000, 512, "f32"), (2049, 1536, "bf16"), (5, 16384, "f32"), (40, 6144, "f32"),
+    (9000, 128, "bf16"), (700, 5120, "f32"),
+]
+
+
+@pytest.mark.parametrize("T,H,wdt", SMALL)
+def test_fwd_small(T, H, wdt):
+    _announce(f"fwd T={T} H={H} w={wdt}")
+    wl = synth.make(T=T, H=H, w_dtype=wdt, seed=T + H)
+    y, rstd = rn.rmsnorm_fwd(dev_bf16(wl.x), dev_w(wl.w), wl.eps)
+    torch.cuda.synchronize()
+    r64, y64 = oracle.fwd(wl.x, wl.w.f64, wl.eps)
+    check_rstd("rstd", rstd.cpu().numpy(), r64)
+    check_bf16_strict("y", host_bits(y), y64)
+
+
+def _bwd_case(wl, det, rstd32):
+    x, dy, w = dev_bf16(wl.x), dev_bf16(wl.dy), dev_w(wl.w)
+    rs = dev_f32(rstd32)
+    dx, dw = rn.rmsnorm_bwd(dy, x, rs, w, deterministic=det)
+    torch.cuda.synchronize()
+    return host_bits(dx), dw.cpu().numpy()
+
+
+@pytest.mark.parametrize("T,H,wdt", SMALL)
+def test_bwd_small(T, H, wdt):
+    _announce(f"bwd T={T} H={H} w={wdt}")
+    wl = synth.make(T=T, H=H, w_dtype=wdt, seed=3 * T + H)
+    r64, r32 = oracle_rstd32(wl.x, wl.w.f64, wl.eps)
+    r32_64 = r32.astype(np.float64)
+    dx64, c64, dw64 = oracle.bwd(wl.dy, wl.x, r32_64, wl.w.f64)
+    _, _, dw64_i = oracle.bwd(wl.dy, wl.x, r64, wl.w.f64, want_dx=False)
+    E = dx_bound(to_f64(wl.x), to_f64(wl.dy), wl.w.f64, r32_64, c64, H)
+    dx_det, dw_det = _bwd_case(wl, True, r32)
+    check_dx("dx det", dx_det, dx64, E)
+    check_dw("dw det (forward's rstd)", dw_det, dw64)
+    check_dw("dw det (FP64 rstd)", dw_det, dw64_i)
+    dx_nd, dw_nd = _bwd_case(wl, False, r32)
+    assert np.array_equal(dx_nd, dx_det), "dx differs between modes"
+    check_dw("dw non-det", dw_nd, dw64)
+    for _ in range(3):
+        dx2, dw2 = _bwd_case(wl, True, r32)
+        assert np.array_equal(dw2.view(np.uint32), dw_det.view(np.uint32)), "det dw not reproducible"
+        assert np.array_equal(dx2, dx_det)
+
+
+@pytest.mark.parametrize("T,H,wdt,with_dres", [(64, 6144, "bf16", True), (333, 6144, "bf16", True),
+                                                (333, 6144, "f32", False), (100, 256, "f32", True)])
+def test_residual_small(T, H, wdt, with_dres):
+    _announce(f"residual T={T} H={H} w={wdt} dres={with_dres}")
+    wl = synth.make(T=T, H=H, w_dtype=wdt, seed=T + 7, residual=True, with_dres=with_dres)
+    h, y, rstd = rn.rmsnorm_residual_fwd(dev_bf16(wl.x), dev_bf16(wl.r), dev_w(wl.w), wl.eps)
+    torch.cuda.synchronize()
+    h_ref = oracle.residual_add(wl.x, wl.r)
+    assert np.array_equal(host_bits(h), h_ref), "h = BF16(x + r) not bit-exact"
+    r64, y64 = oracle.fwd(h_ref, wl.w.f64, wl.eps)
+    check_rstd("rstd", rstd.cpu().numpy(), r64)
+    check_bf16_strict("y", host_bits(y), y64)
+    r32 = oracle.round_f32(r64)
+    dx64, c64, dw64 = oracle.bwd(wl.dy, h_ref, r32.astype(np.float64), wl.w.f64)
+    dres64 = to_f64(wl.dres) if with_dres else None
+    dh64 = dx64 + (dres64 if with_dres else 0.0)
+    E = dx_bound(to_f64(h_ref), to_f64(wl.dy), wl.w.f64, r32.astype(np.float64), c64, H, dres64)
+    outs = []
+    for det in (True, False):
+        dh, dw = rn.rmsnorm_residual_bwd(dev_bf16(wl.dy), dev_bf16(h_ref), dev_f32(r32), dev_w(wl.w),
+                                         dres=dev_bf16(wl.dres) if with_dres else None,
+                                         deterministic=det)
+        torch.cuda.synchronize()
+        outs.append(host_bits(dh))
+        check_dx(f"dh det={det}", outs[-1], dh64, E)
+        check_dw(f"dw det={det}", dw.cpu().numpy(), dw64)
+    assert np.array_equal(outs[0], outs[1])
+
+
+def _strided_case(T, heads, H, row, seed):
+    wl = synth.make(T=T, H=H, w_dtype="f32", seed=seed, heads=heads, strided_row=row)
+    xbuf = dev_bf16(wl.xbuf)
+    xview = xbuf[:, : heads * H].unflatten(1, (heads, H))
+    return wl, xbuf, xview
+
+
+@pytest.mark.parametrize("T,heads,H,row", [(300, 24, 256, 8192), (50, 4, 256, 1024), (7, 3, 512, 2048)])
+def test_strided_heads_small(T, heads, H, row):
+    _announce(f"strided T={T} heads={heads} H={H} row={row}")
+    wl, xbuf, xview = _strided_case(T, heads, H, row, seed=T + heads)
+    w = dev_w(wl.w)
+    y, rstd = rn.rmsnorm_fwd_strided(xview, w, wl.eps)
+    torch.cuda.synchronize()
+    r64, y64 = oracle.fwd(wl.x, wl.w.f64, wl.eps)
+    check_rstd("rstd", rstd.cpu().numpy().reshape(-1), r64)
+    check_bf16_strict("y", host_bits(y).reshape(-1, H), y64)
+    r32 = oracle.round_f32(r64)
+    dx64, c64, dw64 = oracle.bwd(wl.dy, wl.x, r32.astype(np.float64), wl.w.f64)
+    E = dx_bound(to_f64(wl.x), to_f64(wl.dy), wl.w.f64, r32.astype(np.float64), c64, H)
+    dy = dev_bf16(wl.dy).view(T, heads, H)
+    rs = dev_f32(r32).view(T, heads)
+    sentinel = 0x7FC0
+    dxbuf = torch.full((T, row), sentinel, dtype=torch.int16, device=DEV).view(torch.bfloat16)
+    dxview = dxbuf[:, : heads * H].unflatten(1, (heads, H))
+    for det in (True, False):
+        _, dw = rn.rmsnorm_bwd_strided(dy, xview, rs, w, deterministic=det, dx=dxview)
+        torch.cuda.synchronize()
+        full = host_bits(dxbuf)
+        assert np.all(full[:, heads * H:] == sentinel), "gap columns of the dx buffer were written"
+        check_dx(f"dx det={det}", np.ascontiguousarray(full[:, : heads * H]).reshape(-1, H), dx64, E)
+        check_dw(f"dw det={det}", dw.cpu().numpy(), dw64)
+    # strided and contiguous inputs give the same bits (row-local outputs,
+    # same deterministic partition)
+    xc = dev_bf16(wl.x).view(T, heads, H)
+    yc, rc = rn.rmsnorm_fwd_strided(xc, w, wl.eps)
+    dxc, dwc = rn.rmsnorm_bwd_strided(dy, xc, rs, w, deterministic=True)
+    _, dws = rn.rmsnorm_bwd_strided(dy, xview, rs, w, deterministic=True)
+    torch.cuda.synchronize()
+    assert torch.equal(yc.view(torch.int16), y.view(torch.int16))
+    assert torch.equal(rc, rstd)
+    assert np.array_equal(host_bits(dxc).reshape(-1, H),
+                          np.ascontiguousarray(host_bits(dxbuf)[:, : heads * H]).reshape(-1, H))
+    assert torch.equal(dwc.view(torch.int32), dws.view(torch.int32))
+
+
+def test_zero_rows_and_errors():
+    w = torch.ones(64, dtype=torch.float32, device=DEV)
+    x = torch.empty(0, 64, dtype=torch.bfloat16, device=DEV)
+    y, rstd = rn.rmsnorm_fwd(x, w)
+    dx, dw = rn.rmsnorm_bwd(x, x, rstd, w, deterministic=True, dw=torch.full((64,), 7.0, device=DEV))
+    torch.cuda.synchronize()
+    assert torch.all(dw == 0)
+    with pytest.raises(rn.RMSNormError):
+        rn.rmsnorm_fwd(torch.zeros(4, 60, dtype=torch.bfloat16, device=DEV),
+                       torch.ones(60, device=DEV))
+    with pytest.raises(rn.RMSNormError):
+        xx = torch.zeros(4, 64, dtype=torch.bfloat16, device=DEV)
+        rn.rmsnorm_fwd(xx, w, eps=-1.0)
+
+
+def test_nondet_workspace_left_zeroed():
+    wl = synth.make(T=4096, H=1024, w_dtype="bf16", seed=5)
+    _, r32 = oracle_rstd32(wl.x, wl.w.f64, wl.eps)
+    need = rn.rmsnorm_bwd_workspace_bytes(4096, 1024, torch.bfloat16, False)
+    ws = torch.zeros(need + 256, dtype=torch.uint8, device=DEV)
+    off = (-ws.data_ptr()) % 256
+    ws = ws[off:off + need]
+    dws = []
+    for _ in range(3):
+        _, dw = rn.rmsnorm_bwd(dev_bf16(wl.dy), dev_bf16(wl.x), dev_f32(r32), dev_w(wl.w),
+                               deterministic=False, workspace=ws)
+        torch.cuda.synchronize()
+        assert int(ws.count_nonzero()) == 0
+        dws.append(dw.cpu().numpy())
+    _, _, dw64 = oracle.bwd(wl.dy, wl.x, r32.astype(np.float64), wl.w.f64, want_dx=False)
+    for d in dws:
+        check_dw("dw non-det", d, dw64)
+
+
+# --------------------------------------------------------- full-size cases
+
+def _sample_rows(rows: int, extra=None, k: int = 48, seed: int = 123) -> np.ndarray:
+    rng = np.random.default_rng(seed)
+    pick = set(rng.choice(rows, min(k, rows), replace=False).tolist())
+    pick.update([0, rows - 1])
+    if extra is not None:
+        pick.update(int(v) for v in extra[:16])
+    return np.array(sorted(pick))
+
+
+@pytest.mark.parametrize("name", list(synth.CONFIGS))
+def test_full_size_config(name):
+    _announce(f"full-size {name}: generating")
+    wl = synth.config(name, seed=0)
+    rows, H = wl.rows, wl.H
+    w = dev_w(wl.w)
+    res = wl.r is not None
+    # ---------------- forward on the GPU
+    if res:
+        x_in = wl.x
+        h, y, rstd = rn.rmsnorm_residual_fwd(dev_bf16(wl.x), dev_bf16(wl.r), w, wl.eps)
+        torch.cuda.synchronize()
+        h_ref = oracle.residual_add(wl.x, wl.r)
+        assert np.array_equal(host_bits(h), h_ref), "h not bit-exact"
+        del h
+        x_in = h_ref
+    elif wl.xbuf is not None:
+        xbuf = dev_bf16(wl.xbuf)
+        xd = xbuf[:, : wl.heads * H].unflatten(1, (wl.heads, H))
+        y, rstd = rn.rmsnorm_fwd_strided(xd, w, wl.eps)
+        x_in = wl.x
+    elif wl.heads > 1:
+        xd = dev_bf16(wl.x).view(wl.T, wl.heads, H)
+        y, rstd = rn.rmsnorm_fwd_strided(xd, w, wl.eps)
+        x_in = wl.x
+    else:
+        xd = dev_bf16(wl.x)
+        y, rstd = rn.rmsnorm_fwd(xd, w, wl.eps)
+        x_in = wl.x
+    torch.cuda.synchronize()
+    _announce(f"full-size {name}: oracle forward over all rows")
+    r64, r32 = oracle_rstd32(x_in, wl.w.f64, wl.eps)
+    check_rstd("rstd (all rows)", rstd.cpu().numpy().reshape(-1), r64)
+    sample = _sample_rows(rows, wl.heavy_rows)
+    _, y64 = oracle.fwd(x_in[sample], wl.w.f64, wl.eps)
+    ybits = host_bits(y).reshape(rows, H)
+    check_bf16_strict("y (sampled rows)", ybits[sample], y64)
+    del y, ybits
+    # ---------------- backward on the GPU, fed the oracle's FP32 rstd
+    rs = dev_f32(r32)
+    dy = dev_bf16(wl.dy)
+    r32_64 = r32.astype(np.float64)
+    _announce(f"full-size {name}: oracle dw over all rows")
+    _, _, dw64 = oracle.bwd(wl.dy, x_in, r32_64, wl.w.f64, want_dx=False)
+    _, _, dw64_i = oracle.bwd(wl.dy, x_in, r64, wl.w.f64, want_dx=False)
+    dx64, c64, _ = oracle.bwd(wl.dy[sample], x_in[sample], r32_64[sample], wl.w.f64)
+    dres64 = to_f64(wl.dres[sample]) if (res and wl.dres is not None) else None
+    E = dx_bound(to_f64(x_in[sample]), to_f64(wl.dy[sample]), wl.w.f64, r32_64[sample], c64, H, dres64)
+    ref_dx = dx64 + (dres64 if dres64 is not None else 0.0)
+    def run_bwd(det):
+        if res:
+            dx, dw = rn.rmsnorm_residual_bwd(dy, dev_bf16(x_in), rs, w,
+                                             dres=dev_bf16(wl.dres) if wl.dres is not None else None,
+                                             deterministic=det)
+            torch.cuda.synchronize()
+            return host_bits(dx).reshape(rows, H), dw.cpu().numpy()
+        if wl.xbuf is not None:
+            sentinel = 0x7FC0
+            dxbuf = torch.full(wl.xbuf.shape, sentinel, dtype=torch.int16, device=DEV).view(torch.bfloat16)
+            dxv = dxbuf[:, : wl.heads * H].unflatten(1, (wl.heads, H))
+            _, dw = rn.rmsnorm_bwd_strided(dy.view(wl.T, wl.heads, H), xd, rs.view(wl.T, wl.heads), w,
+                                           deterministic=det, dx=dxv)
+            torch.cuda.synchronize()
+            full = host_bits(dxbuf)
+            assert np.all(full[:, wl.heads * H:] == sentinel), "gap columns written"
+            return np.ascontiguousarray(full[:, : wl.heads * H]).reshape(rows, H), dw.cpu().numpy()
+        if wl.heads > 1:
+            dx, dw = rn.rmsnorm_bwd_strided(dy.view(wl.T, wl.heads, H), xd, rs.view(wl.T, wl.heads), w,
+                                            deterministic=det)
+            torch.cuda.synchronize()
+            return host_bits(dx).reshape(rows, H), dw.cpu().numpy()
+        dx, dw = rn.rmsnorm_bwd(dy, xd, rs, w, deterministic=det)
+        torch.cuda.synchronize()
+        return host_bits(dx), dw.cpu().numpy()
+
+    dx_bits = {}
+    det_dw_bits = None
+    for det in (True, False):
+        _announce(f"full-size {name}: backward det={det}")
+        dxb, dwn = run_bwd(det)
+        n_ex = check_dx(f"dx det={det} (sampled rows)", dxb[sample], ref_dx, E)
+        f2 = check_dw(f"dw det={det} (forward's rstd)", dwn, dw64)
+        f1 = check_dw(f"dw det={det} (FP64 rstd)", dwn, dw64_i)
+        _announce(f"  dx exempted={n_ex} dw worst/budget={f2:.4f} (fp64-rstd form {f1:.4f})")
+        dx_bits[det] = dxb[sample].copy()
+        if det:
+            det_dw_bits = dwn.view(np.uint32).copy()
+        del dxb
+    assert np.array_equal(dx_bits[True], dx_bits[False]), "dx differs between modes"
+    # deterministic dw: bit-identical over 10 runs
+    for i in range(10):
+        _, dwn = run_bwd(True)
+        assert np.array_equal(dwn.view(np.uint32), det_dw_bits), f"deterministic dw changed on run {i}"
+    # non-deterministic dw: inside the budget on every run
+    for i in range(3):
+        _, dwn = run_bwd(False)
+        check_dw(f"dw non-det run {i}", dwn, dw64)
