@@ -24,7 +24,8 @@ __all__ = [
     "rmsnorm_fwd", "rmsnorm_fwd_strided", "rmsnorm_residual_fwd", "rmsnorm_bwd",
     "rmsnorm_bwd_strided", "rmsnorm_residual_bwd", "rmsnorm_bwd_workspace_bytes",
     "rmsnorm_workspace_init", "rmsnorm_status_string", "rmsnorm_route_query",
-    "rmsnorm_timing_enable", "rmsnorm_timing_read", "RMSNormError", "View",
+    "rmsnorm_route_override", "rmsnorm_timing_enable", "rmsnorm_timing_read",
+    "RMSNormError", "View",
 ]
 
 
@@ -131,19 +132,16 @@ def rmsnorm_workspace_init(ws: torch.Tensor) -> None:
                                                   _stream(ws.device)))
 
 
-def _workspace(dev: torch.device, nbytes: int, deterministic: bool) -> Optional[torch.Tensor]:
-    """Per (device, stream) workspace. The non-deterministic kernels need it
-    zero-filled on first use and leave it zero-filled."""
+def _workspace(dev: torch.device, nbytes: int) -> Optional[torch.Tensor]:
+    """Scratch workspace kept per (device, stream); the kernels need no
+    initialisation of it."""
     if nbytes == 0:
         return None
-    key = (dev, torch.cuda.current_stream(dev).cuda_stream, bool(deterministic))
+    key = (dev, torch.cuda.current_stream(dev).cuda_stream)
     ws = _WS_CACHE.get(key)
     if ws is None or ws.numel() < nbytes:
-        ws = torch.empty(max(nbytes, 1 << 20) + 256, dtype=torch.uint8, device=dev)
-        off = (-ws.data_ptr()) % 256
-        ws = ws[off:]
-        if not deterministic:
-            rmsnorm_workspace_init(ws)
+        raw = torch.empty(max(nbytes, 1 << 20) + 256, dtype=torch.uint8, device=dev)
+        ws = raw[(-raw.data_ptr()) % 256:]
         _WS_CACHE[key] = ws
     return ws
 
@@ -158,7 +156,7 @@ def rmsnorm_bwd(dy: torch.Tensor, x: torch.Tensor, rstd: torch.Tensor, w: torch.
     dx = torch.empty_like(x) if dx is None else dx
     dw = torch.empty(H, dtype=torch.float32, device=x.device) if dw is None else dw
     need = rmsnorm_bwd_workspace_bytes(T, H, w.dtype, deterministic)
-    ws = workspace if workspace is not None else _workspace(x.device, need, deterministic)
+    ws = workspace if workspace is not None else _workspace(x.device, need)
     nbytes = 0 if ws is None else ws.numel() * ws.element_size()
     _lib.check(_lib.load().rmsnorm_bwd(_ptr(dy), _ptr(x), _ptr(rstd), _ptr(w), _wdtype(w),
                                        int(bool(deterministic)), _ptr(dx), _ptr(dw), T, H,
@@ -179,7 +177,7 @@ def rmsnorm_bwd_strided(dy: torch.Tensor, x: torch.Tensor, rstd: torch.Tensor, w
         dx = torch.empty(x.shape, dtype=torch.bfloat16, device=x.device)
     dw = torch.empty(xv.H, dtype=torch.float32, device=x.device) if dw is None else dw
     need = rmsnorm_bwd_workspace_bytes(rows, xv.H, w.dtype, deterministic)
-    ws = workspace if workspace is not None else _workspace(x.device, need, deterministic)
+    ws = workspace if workspace is not None else _workspace(x.device, need)
     nbytes = 0 if ws is None else ws.numel() * ws.element_size()
     _lib.check(_lib.load().rmsnorm_bwd_strided(_ptr(dy), _view(dy), _ptr(x), xv, _ptr(rstd),
                                                _ptr(w), _wdtype(w), int(bool(deterministic)),
@@ -199,7 +197,7 @@ def rmsnorm_residual_bwd(dy: torch.Tensor, h: torch.Tensor, rstd: torch.Tensor, 
     dh = torch.empty_like(h) if dh is None else dh
     dw = torch.empty(H, dtype=torch.float32, device=h.device) if dw is None else dw
     need = rmsnorm_bwd_workspace_bytes(T, H, w.dtype, deterministic)
-    ws = workspace if workspace is not None else _workspace(h.device, need, deterministic)
+    ws = workspace if workspace is not None else _workspace(h.device, need)
     nbytes = 0 if ws is None else ws.numel() * ws.element_size()
     _lib.check(_lib.load().rmsnorm_residual_bwd(_ptr(dy), _ptr(h), _ptr(dres), _ptr(rstd), _ptr(w),
                                                 _wdtype(w), int(bool(deterministic)), _ptr(dh),
@@ -223,6 +221,18 @@ def rmsnorm_route_query(op: str, rows: int, H: int, w_dtype: torch.dtype = torch
                                                int(bool(deterministic)), int(bool(residual)),
                                                ctypes.byref(info)))
     return info.as_dict()
+
+
+def rmsnorm_route_override(op: str, **knobs) -> None:
+    """Set (or, with no knobs, clear) the tuning override of op 'fwd'/'bwd'.
+    Knobs: vec_per_lane, unroll, rows_per_block, blocks_per_cu, partial_f64
+    (1 FP64, 2 FP32), kind (RMSN_KIND_BWD_ROW_DET/_ATOMIC, non-det only)."""
+    o = 0 if op == "fwd" else 1
+    if not knobs:
+        _lib.check(_lib.load().rmsnorm_route_override(o, None))
+        return
+    k = _lib.RouteKnobs(**knobs)
+    _lib.check(_lib.load().rmsnorm_route_override(o, ctypes.byref(k)))
 
 
 def rmsnorm_timing_enable(enable: bool = True) -> None:

@@ -38,7 +38,8 @@ EXPORTS = [
     "rmsnorm_fwd", "rmsnorm_fwd_strided", "rmsnorm_residual_fwd",
     "rmsnorm_bwd_workspace_bytes", "rmsnorm_workspace_init", "rmsnorm_bwd",
     "rmsnorm_bwd_strided", "rmsnorm_residual_bwd", "rmsnorm_status_string",
-    "rmsnorm_route_query", "rmsnorm_timing_enable", "rmsnorm_timing_read",
+    "rmsnorm_route_query", "rmsnorm_route_override", "rmsnorm_timing_enable",
+    "rmsnorm_timing_read",
 ]
 
 
@@ -50,12 +51,19 @@ class View(ctypes.Structure):
 class RouteInfo(ctypes.Structure):
     _fields_ = [("kind", ctypes.c_int), ("vec_per_lane", ctypes.c_int),
                 ("lanes_per_row", ctypes.c_int), ("rows_per_block", ctypes.c_int),
-                ("block_threads", ctypes.c_int), ("partial_f64", ctypes.c_int),
+                ("unroll", ctypes.c_int), ("block_threads", ctypes.c_int),
+                ("partial_f64", ctypes.c_int), ("reduce_threads", ctypes.c_int),
                 ("grid", ctypes.c_int64), ("partials", ctypes.c_int64),
                 ("reduce_grid", ctypes.c_int64)]
 
     def as_dict(self):
         return {f: getattr(self, f) for f, _ in self._fields_}
+
+
+class RouteKnobs(ctypes.Structure):
+    _fields_ = [("vec_per_lane", ctypes.c_int), ("unroll", ctypes.c_int),
+                ("rows_per_block", ctypes.c_int), ("blocks_per_cu", ctypes.c_int),
+                ("partial_f64", ctypes.c_int), ("kind", ctypes.c_int)]
 
 
 class RMSNormError(RuntimeError):
@@ -90,6 +98,7 @@ def load() -> ctypes.CDLL:
         "rmsnorm_residual_bwd": [p, p, p, p, p, i32, i32, p, p, i64, i64, p, sz, p],
         "rmsnorm_status_string": [i32],
         "rmsnorm_route_query": [i32, i64, i64, i32, i32, i32, ctypes.POINTER(RouteInfo)],
+        "rmsnorm_route_override": [i32, ctypes.POINTER(RouteKnobs)],
         "rmsnorm_timing_enable": [i32],
         "rmsnorm_timing_read": [ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_double), i32],
     }

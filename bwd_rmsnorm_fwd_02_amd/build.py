@@ -15,10 +15,12 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libbwd_rmsnorm.so")
-SOURCES = ["fwd.hip", "bwd.hip", "route.cpp", "api.cpp"]
+SOURCES = ["fwd_bf16w.hip", "fwd_f32w.hip", "bwd_bf16w.hip", "bwd_f32w.hip", "reduce.hip",
+           "route.cpp", "api.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-# Packed FP32 instructions are disabled for every HIP source.
+# Packed FP32 vector instructions are disabled for every HIP source (the
+# compiler would otherwise form them from plain float code).
 COMMON = [
     "-std=c++17", "-O3", "-fPIC", "--offload-arch=gfx950",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

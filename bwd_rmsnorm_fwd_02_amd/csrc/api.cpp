@@ -299,9 +299,14 @@ int bwd_impl(const void* dy, const rmsn_view_t& dyv, const void* x, const rmsn_v
         timer_end(RMSN_TIMER_DW_REDUCE, s);
         return st;
     }
-    // atomic route: accumulator [H] doubles then the ticket
+    // atomic route: accumulator [H] doubles then the ticket, cleared first so
+    // the workspace needs no initialisation by the caller
     p.acc = static_cast<double*>(ws);
     p.ticket = reinterpret_cast<unsigned int*>(static_cast<char*>(ws) + (((size_t)H * 8 + 255) & ~(size_t)255));
+    timer_begin(RMSN_TIMER_INIT, s);
+    st = launch_fill_zero(ws, rt.workspace, s);
+    timer_end(RMSN_TIMER_INIT, s);
+    if (st != RMSN_OK) return st;
     timer_begin(RMSN_TIMER_BWD_ROW, s);
     st = launch_bwd_row(p, rt, wdt, residual, s);
     timer_end(RMSN_TIMER_BWD_ROW, s);
@@ -408,6 +413,10 @@ int rmsnorm_route_query(int op, int64_t rows, int64_t H, rmsn_dtype_t w_dtype, i
     const int st = route(op, rows, H, w_dtype, deterministic, residual, &rt);
     *out = rt.r;
     return st;
+}
+
+int rmsnorm_route_override(int op, const rmsn_route_knobs_t* knobs) {
+    return set_route_knobs(op, knobs);
 }
 
 int rmsnorm_timing_enable(int enable) {

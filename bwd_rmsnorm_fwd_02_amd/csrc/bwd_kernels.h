@@ -1,0 +1,498 @@
+// RMSNorm backward for gfx950 (kernel templates): dx per row, and dw as a
+// column sum over rows.
+//
+// Per row (flashinfer PR "fix(cake_rmsnorm): sm_100a and sm_107a dw-accuracy
+// backward routes", opening description): with xhat = x * rstd and
+// g = dy * w, c = mean(g * xhat), dx = BF16(rstd * (g - xhat * c)); in the
+// residual form ("Key": combined grad) dh = BF16(dres + that gradient). dx
+// is computed by one function (bwd_compute) for every kernel and mode here; for
+// a given launch shape it is bit-identical between deterministic and
+// non-deterministic calls.
+//
+// dw_j = sum over rows of dy * xhat. Each lane owns fixed columns (the same
+// 16-byte vectors it owns in every row) and accumulates dy*x*rstd in FP64
+// registers: dy*x is exact in FP32 (two 8-bit significands), and the FP64
+// fused multiply-add by the row's rstd loses nothing that matters. gfx950
+// runs FP64 FMA at the rate of unpacked FP32, so this costs three vector
+// operations per element and replaces the compensated FP32 sums (TwoSum
+// plus periodic FP64 fold) that the pages use on hardware with slow FP64.
+//
+// How the per-block sums meet (the only difference between the modes):
+// * deterministic: block b owns the contiguous row range
+//   [b*rows/P, (b+1)*rows/P), where P (the grid) is a function of the shape
+//   only; row slots inside the block are combined in slot order; the block
+//   writes its partial row; k_dw_reduce then sums the P partials in a fixed
+//   order. No step depends on scheduling or on the CU count.
+// * atomic (non-deterministic): the same blocks add their sums into an FP64
+//   accumulator with hardware atomics; the last block to finish (a ticket
+//   counter) converts it to FP32 dw.
+// * small T: one launch of k_bwd_small — column tasks sum whole columns over
+//   every row in a fixed row order while row tasks produce dx.
+#pragma once
+
+#include "rmsn_device.h"
+
+namespace rmsn {
+
+enum { kModePartF32 = 0, kModePartF64 = 1, kModeAtomic = 2 };
+
+// Rows a row group holds at once: x, dy, (dres), rstd for U rows.
+template <int NV, int U, bool RES>
+struct BwdTile {
+    uint4 x[U][NV];
+    uint4 dy[U][NV];
+    uint4 dres[U][NV];  // RES with a residual gradient only
+    float rs[U];
+};
+
+// Issue the loads of rows r0 + slot + k*rpb (k < U). Every lane issues the
+// same loads: rows at or past rend and vectors past the row end are clamped
+// to the last valid ones and their values ignored, so there are no branches
+// around memory operations (branches there make the compiler's wait counting
+// fall back to waiting for everything). Without a residual gradient the dres
+// slot reloads dy, which stays unused.
+template <int NV, int U, bool RES>
+__device__ __forceinline__ void bwd_load(const BwdParams& p, int64_t r0, int64_t rend, int slot,
+                                         int lr, BwdTile<NV, U, RES>& t) {
+#pragma unroll
+    for (int k = 0; k < U; ++k) {
+        int64_t r = r0 + slot + (int64_t)k * p.rpb;
+        if (r > rend - 1) r = rend - 1;
+        const int64_t ox = row_offset(r, p.heads, p.ax);
+        const int64_t ody = row_offset(r, p.heads, p.ady);
+        int64_t ores = 0;
+        const uint16_t* rsrc = p.dy;
+        if constexpr (RES) {
+            if (p.dres) {
+                ores = row_offset(r, p.heads, p.ares);
+                rsrc = p.dres;
+            } else {
+                ores = ody;
+            }
+        }
+#pragma unroll
+        for (int v = 0; v < NV; ++v) {
+            int vi = lr + v * p.tpr;
+            if (vi > p.nvec - 1) vi = p.nvec - 1;
+            const int64_t c = (int64_t)vi * kVec;
+            t.x[k][v] = ld16(p.x + ox + c);
+            t.dy[k][v] = ld16(p.dy + ody + c);
+            if constexpr (RES) t.dres[k][v] = ld16(rsrc + ores + c);
+        }
+        t.rs[k] = p.rstd[r];
+    }
+}
+
+template <int NV, int U, bool RES>
+__device__ __forceinline__ void bwd_ready(const BwdTile<NV, U, RES>& t) {
+#pragma unroll
+    for (int k = 0; k < U; ++k) {
+#pragma unroll
+        for (int v = 0; v < NV; ++v) {
+            use_now(t.x[k][v]);
+            use_now(t.dy[k][v]);
+            if constexpr (RES) use_now(t.dres[k][v]);
+        }
+        use_now(t.rs[k]);
+    }
+}
+
+// Row-group sums of U per-lane FP32 values. WIDE rows span several waves
+// and exchange wave sums through LDS, double-buffered by `buf` so that one
+// LDS-only barrier per iteration suffices. The order of every sum is fixed.
+template <int U, bool WIDE>
+__device__ __forceinline__ void row_sums(float (&v)[U], const BwdParams& p, int slot, int lr,
+                                         float* red, int& buf) {
+    if constexpr (WIDE) {
+        const int wpr = p.tpr >> 6;
+        const int wave = lr >> 6;
+#pragma unroll
+        for (int k = 0; k < U; ++k) {
+            const float a = group_sum<64>(v[k]);
+            if ((lr & 63) == 0 && slot < p.rpb) red[((buf * p.rpb + slot) * U + k) * wpr + wave] = a;
+        }
+        lds_barrier();
+#pragma unroll
+        for (int k = 0; k < U; ++k) {
+            float t = 0.f;
+            if (slot < p.rpb)
+                for (int i = 0; i < wpr; ++i) t += red[((buf * p.rpb + slot) * U + k) * wpr + i];
+            v[k] = t;
+        }
+        buf ^= 1;
+    } else {
+#pragma unroll
+        for (int k = 0; k < U; ++k) v[k] = group_sum_rt(v[k], p.tpr);
+    }
+}
+
+// The backward of the rows held in a tile, up to the stores: dx (or dh)
+// packed into `out`, and, if ACC, dy*x*rstd added into acc for rows below
+// rend. No memory operation happens here except the LDS exchange.
+template <int NV, int U, bool RES, bool WIDE, bool ACC>
+__device__ __forceinline__ void bwd_compute(const BwdParams& p, int64_t r0, int64_t rend,
+                                            int slot, int lr, const float (&wv)[NV][8],
+                                            const bool (&vok)[NV], const BwdTile<NV, U, RES>& t,
+                                            double (&acc)[NV][8], uint4 (&out)[U][NV], float* red,
+                                            int& buf) {
+    float dot[U];
+#pragma unroll
+    for (int k = 0; k < U; ++k) {
+        dot[k] = 0.f;
+#pragma unroll
+        for (int v = 0; v < NV; ++v) {
+            float xf[8], dyf[8];
+            unpack8(t.x[k][v], xf);
+            unpack8(t.dy[k][v], dyf);
+            float s = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) s = __builtin_fmaf(dyf[e] * wv[v][e], xf[e], s);
+            if (vok[v]) dot[k] += s;
+        }
+    }
+    row_sums<U, WIDE>(dot, p, slot, lr, red, buf);
+#pragma unroll
+    for (int k = 0; k < U; ++k) {
+        const int64_t r = r0 + slot + (int64_t)k * p.rpb;
+        const bool live = (slot < p.rpb) && (r < rend);
+        const float rs = t.rs[k];
+        // c = (1/H) sum_j g_j * xhat_j = rstd * sum_j g_j x_j / H
+        const float c = (dot[k] * rs) / (float)p.H;
+        const double rs64 = (double)rs;
+#pragma unroll
+        for (int v = 0; v < NV; ++v) {
+            float xf[8], dyf[8], o[8];
+            unpack8(t.x[k][v], xf);
+            unpack8(t.dy[k][v], dyf);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float g = dyf[e] * wv[v][e];
+                const float xh = xf[e] * rs;
+                o[e] = __builtin_fmaf(-xh, c, g) * rs;
+            }
+            if constexpr (RES) {
+                if (p.dres) {
+                    float d[8];
+                    unpack8(t.dres[k][v], d);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) o[e] += d[e];
+                }
+            }
+            out[k][v] = pack8(o);
+            if constexpr (ACC) {
+                if (live && vok[v]) {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        acc[v][e] = __builtin_fma((double)(dyf[e] * xf[e]), rs64, acc[v][e]);
+                }
+            }
+        }
+    }
+}
+
+// Store the dx (or dh) rows of a tile that lie below rend.
+template <int NV, int U>
+__device__ __forceinline__ void bwd_store(const BwdParams& p, int64_t r0, int64_t rend, int slot,
+                                          int lr, const bool (&vok)[NV], const uint4 (&out)[U][NV]) {
+#pragma unroll
+    for (int k = 0; k < U; ++k) {
+        const int64_t r = r0 + slot + (int64_t)k * p.rpb;
+        if (slot >= p.rpb || r >= rend) continue;
+        const int64_t odx = row_offset(r, p.heads, p.adx);
+#pragma unroll
+        for (int v = 0; v < NV; ++v) {
+            if (!vok[v]) continue;
+            st16(p.dx + odx + (int64_t)(lr + v * p.tpr) * kVec, out[k][v]);
+        }
+    }
+}
+
+template <int NV, typename WT>
+__device__ __forceinline__ void load_weights(const BwdParams& p, int slot, int lr,
+                                             float (&wv)[NV][8], bool (&vok)[NV]) {
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+        const int vi = lr + v * p.tpr;
+        vok[v] = (slot < p.rpb) && (vi < p.nvec);
+        if (vok[v]) {
+            load_w8<WT>(p.w, vi, wv[v]);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) wv[v][e] = 0.f;
+        }
+    }
+}
+
+// Large-T row kernel: dx for the block's rows plus the block's dw sums.
+// Block b owns rows [b*rows/P, (b+1)*rows/P); each iteration a row group
+// takes U rows of it. With U <= 2 the next iteration's rows are loaded
+// before the current ones are processed.
+template <int NV, int U, typename WT, bool RES, bool WIDE, int MODE>
+__global__ void __launch_bounds__(WIDE ? (NV * U >= 4 ? 512 : 1024) : 256) k_bwd_row(BwdParams p) {
+    constexpr bool PF = U <= 2;
+    extern __shared__ double lds_bwd[];
+    const int tid = threadIdx.x;
+    const int slot = tid / p.tpr;
+    const int lr = tid - slot * p.tpr;
+    // LDS: [H] doubles for the slot combine, then the row-sum exchange area
+    double* comb = lds_bwd;
+    float* red = reinterpret_cast<float*>(lds_bwd + (p.rpb > 1 ? p.H : 0));
+
+    float wv[NV][8];
+    bool vok[NV];
+    load_weights<NV, WT>(p, slot, lr, wv, vok);
+
+    double acc[NV][8];
+#pragma unroll
+    for (int v = 0; v < NV; ++v)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[v][e] = 0.0;
+
+    const int64_t P = gridDim.x;
+    const int64_t b = blockIdx.x;
+    const int64_t rbeg = (b * p.rows) / P;
+    const int64_t rend = ((b + 1) * p.rows) / P;
+    const int64_t per_iter = (int64_t)p.rpb * U;
+    const int64_t nit = (rend - rbeg + per_iter - 1) / per_iter;
+    int buf = 0;
+    if (nit > 0) {
+        BwdTile<NV, U, RES> cur;
+        BwdTile<NV, PF ? U : 1, RES> nxt;
+        bwd_load<NV, U, RES>(p, rbeg, rend, slot, lr, cur);
+        bwd_ready<NV, U, RES>(cur);
+#pragma unroll 1
+        for (int64_t it = 0; it < nit; ++it) {
+            const int64_t r0 = rbeg + it * per_iter;
+            if constexpr (PF) bwd_load<NV, U, RES>(p, r0 + per_iter, rend, slot, lr, nxt);
+            uint4 out[U][NV];
+            bwd_compute<NV, U, RES, WIDE, true>(p, r0, rend, slot, lr, wv, vok, cur, acc, out, red, buf);
+            // The next tile must be complete before its registers take over;
+            // the wait lands before this iteration's stores are issued.
+            if constexpr (PF) {
+                bwd_ready<NV, U, RES>(nxt);
+                cur = nxt;
+            }
+            bwd_store<NV, U>(p, r0, rend, slot, lr, vok, out);
+            if constexpr (!PF) {
+                if (it + 1 < nit) bwd_load<NV, U, RES>(p, r0 + per_iter, rend, slot, lr, cur);
+            }
+        }
+    }
+
+    // Combine the row slots in slot order: acc(0) + acc(1) + ... (fixed).
+    if (p.rpb > 1) {
+        for (int s = 1; s < p.rpb; ++s) {
+            __syncthreads();
+            if (slot == s) {
+#pragma unroll
+                for (int v = 0; v < NV; ++v)
+                    if (vok[v])
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) comb[(lr + v * p.tpr) * kVec + e] = acc[v][e];
+            }
+            __syncthreads();
+            if (slot == 0) {
+#pragma unroll
+                for (int v = 0; v < NV; ++v)
+                    if (vok[v])
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) acc[v][e] += comb[(lr + v * p.tpr) * kVec + e];
+            }
+        }
+    }
+
+    if constexpr (MODE == kModePartF64 || MODE == kModePartF32) {
+        if (slot == 0) {
+#pragma unroll
+            for (int v = 0; v < NV; ++v) {
+                if (!vok[v]) continue;
+                const int64_t col = (int64_t)(lr + v * p.tpr) * kVec;
+                if constexpr (MODE == kModePartF64) {
+                    double2* dst = reinterpret_cast<double2*>(static_cast<double*>(p.partial) + b * p.H + col);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) dst[e] = make_double2(acc[v][2 * e], acc[v][2 * e + 1]);
+                } else {
+                    float4* dst = reinterpret_cast<float4*>(static_cast<float*>(p.partial) + b * p.H + col);
+                    dst[0] = make_float4((float)acc[v][0], (float)acc[v][1], (float)acc[v][2], (float)acc[v][3]);
+                    dst[1] = make_float4((float)acc[v][4], (float)acc[v][5], (float)acc[v][6], (float)acc[v][7]);
+                }
+            }
+        }
+    } else if constexpr (MODE == kModeAtomic) {
+        if (slot == 0) {
+#pragma unroll
+            for (int v = 0; v < NV; ++v) {
+                if (!vok[v]) continue;
+                const int64_t col = (int64_t)(lr + v * p.tpr) * kVec;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) unsafeAtomicAdd(p.acc + col + e, acc[v][e]);
+            }
+        }
+        __threadfence();
+        __syncthreads();
+        __shared__ unsigned int last;
+        if (tid == 0) last = (atomicAdd(p.ticket, 1u) == (unsigned int)(P - 1)) ? 1u : 0u;
+        __syncthreads();
+        if (last) {
+            __threadfence();
+            for (int j = tid; j < p.H; j += blockDim.x) {
+                unsigned long long old =
+                    atomicExch(reinterpret_cast<unsigned long long*>(p.acc + j), 0ull);
+                p.dw[j] = (float)__longlong_as_double((long long)old);
+            }
+            if (tid == 0) atomicExch(p.ticket, 0u);
+        }
+    }
+}
+
+// Small-T backward, one launch. Blocks [0, ncol_blocks) are column tasks:
+// thread (vector column v, split s) sums rows [s*T/S, (s+1)*T/S) in order,
+// and the S split sums are added in split order. The other blocks are row
+// tasks computing dx with the shared row code.
+template <int NV, typename WT, bool RES>
+__global__ void __launch_bounds__(256) k_bwd_small(BwdParams p) {
+    extern __shared__ double lds_small[];
+    const int tid = threadIdx.x;
+    if ((int)blockIdx.x < p.ncol_blocks) {
+        const int S = p.col_splits;
+        const int vb = blockDim.x / S;  // vector columns per block
+        const int lv = tid % vb;
+        const int s = tid / vb;
+        const int v = blockIdx.x * vb + lv;
+        double a[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) a[e] = 0.0;
+        if (v < p.nvec) {
+            const int64_t r0 = ((int64_t)s * p.rows) / S;
+            const int64_t r1 = ((int64_t)(s + 1) * p.rows) / S;
+            for (int64_t r = r0; r < r1; ++r) {
+                const int64_t ox = row_offset(r, p.heads, p.ax) + (int64_t)v * kVec;
+                const int64_t ody = row_offset(r, p.heads, p.ady) + (int64_t)v * kVec;
+                float xf[8], dyf[8];
+                unpack8(ld16(p.x + ox), xf);
+                unpack8(ld16(p.dy + ody), dyf);
+                const double rs = (double)p.rstd[r];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) a[e] = __builtin_fma((double)(dyf[e] * xf[e]), rs, a[e]);
+            }
+        }
+        double* sm = lds_small;  // [S][vb*8]
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sm[(s * vb + lv) * 8 + e] = a[e];
+        __syncthreads();
+        if (s == 0 && v < p.nvec) {
+            for (int q = 1; q < S; ++q)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) a[e] += sm[(q * vb + lv) * 8 + e];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) p.dw[(int64_t)v * kVec + e] = (float)a[e];
+        }
+        return;
+    }
+    // Row task: rows [rb, rb + rpb), one per row group.
+    const int slot = tid / p.tpr;
+    const int lr = tid - slot * p.tpr;
+    float wv[NV][8];
+    bool vok[NV];
+    load_weights<NV, WT>(p, slot, lr, wv, vok);
+    double acc[NV][8];
+    float* red = reinterpret_cast<float*>(lds_small);
+    int buf = 0;
+    const int64_t rb = (int64_t)(blockIdx.x - p.ncol_blocks) * p.rpb;
+    BwdTile<NV, 1, RES> t;
+    uint4 out[1][NV];
+    bwd_load<NV, 1, RES>(p, rb, p.rows, slot, lr, t);
+    if (p.tpr > 64)
+        bwd_compute<NV, 1, RES, true, false>(p, rb, p.rows, slot, lr, wv, vok, t, acc, out, red, buf);
+    else
+        bwd_compute<NV, 1, RES, false, false>(p, rb, p.rows, slot, lr, wv, vok, t, acc, out, red, buf);
+    bwd_store<NV, 1>(p, rb, p.rows, slot, lr, vok, out);
+}
+
+// ----------------------------------------------------------------- launchers
+
+inline size_t bwd_row_lds_bytes(const rmsn_route_t& r, int H) {
+    size_t lds = r.rows_per_block > 1 ? sizeof(double) * (size_t)H : 0;
+    if (r.lanes_per_row > 64)
+        lds += sizeof(float) * 2 * (size_t)r.rows_per_block * r.unroll * (r.lanes_per_row / 64);
+    return lds;
+}
+
+template <int NV, int U, typename WT, bool RES, bool WIDE>
+static int launch_row_mode(const BwdParams& p, const Route& rt, size_t lds, hipStream_t s) {
+    dim3 grid((unsigned)rt.r.grid), block((unsigned)rt.r.block_threads);
+    if (rt.r.kind == RMSN_KIND_BWD_ROW_ATOMIC) {
+        if constexpr (NV == 1 && U <= 2)
+            hipLaunchKernelGGL((k_bwd_row<NV, U, WT, RES, WIDE, kModeAtomic>), grid, block, lds, s, p);
+        else
+            return RMSN_ERR_SHAPE;
+    } else if (rt.r.partial_f64) {
+        hipLaunchKernelGGL((k_bwd_row<NV, U, WT, RES, WIDE, kModePartF64>), grid, block, lds, s, p);
+    } else {
+        hipLaunchKernelGGL((k_bwd_row<NV, U, WT, RES, WIDE, kModePartF32>), grid, block, lds, s, p);
+    }
+    return hipGetLastError() == hipSuccess ? RMSN_OK : RMSN_ERR_LAUNCH;
+}
+
+template <int NV, int U, typename WT, bool RES>
+static int launch_row_t(const BwdParams& p, const Route& rt, hipStream_t s) {
+    const size_t lds = bwd_row_lds_bytes(rt.r, p.H);
+    if (rt.r.lanes_per_row > 64) return launch_row_mode<NV, U, WT, RES, true>(p, rt, lds, s);
+    return launch_row_mode<NV, U, WT, RES, false>(p, rt, lds, s);
+}
+
+// (NV, U) pairs compiled: NV * U <= 8, NV <= 2.
+template <typename WT, bool RES>
+static int launch_row_shape(const BwdParams& p, const Route& rt, hipStream_t s) {
+    const int nv = rt.r.vec_per_lane, u = rt.r.unroll;
+    if (nv == 1) {
+        switch (u) {
+            case 1: return launch_row_t<1, 1, WT, RES>(p, rt, s);
+            case 2: return launch_row_t<1, 2, WT, RES>(p, rt, s);
+            case 4: return launch_row_t<1, 4, WT, RES>(p, rt, s);
+            case 8: return launch_row_t<1, 8, WT, RES>(p, rt, s);
+        }
+    } else if (nv == 2) {
+        switch (u) {
+            case 1: return launch_row_t<2, 1, WT, RES>(p, rt, s);
+            case 2: return launch_row_t<2, 2, WT, RES>(p, rt, s);
+            case 4: return launch_row_t<2, 4, WT, RES>(p, rt, s);
+        }
+    }
+    return RMSN_ERR_SHAPE;
+}
+
+template <int NV, typename WT, bool RES>
+static int launch_small_t(const BwdParams& p, const Route& rt, hipStream_t s) {
+    const rmsn_route_t& r = rt.r;
+    const int vb = 256 / p.col_splits;
+    size_t lds = sizeof(double) * (size_t)p.col_splits * vb * 8;
+    const size_t lds_red =
+        sizeof(float) * 2 * r.rows_per_block * (r.lanes_per_row > 64 ? r.lanes_per_row / 64 : 1);
+    if (lds_red > lds) lds = lds_red;
+    hipLaunchKernelGGL((k_bwd_small<NV, WT, RES>), dim3((unsigned)r.grid), dim3(256), lds, s, p);
+    return hipGetLastError() == hipSuccess ? RMSN_OK : RMSN_ERR_LAUNCH;
+}
+
+template <typename WT, bool RES>
+static int launch_small_shape(const BwdParams& p, const Route& rt, hipStream_t s) {
+    switch (rt.r.vec_per_lane) {
+        case 1: return launch_small_t<1, WT, RES>(p, rt, s);
+        case 2: return launch_small_t<2, WT, RES>(p, rt, s);
+        case 4: return launch_small_t<4, WT, RES>(p, rt, s);
+        case 8: return launch_small_t<8, WT, RES>(p, rt, s);
+        default: return RMSN_ERR_SHAPE;
+    }
+}
+
+template <typename WT>
+static int launch_bwd_row_wt(const BwdParams& p, const Route& rt, bool residual, hipStream_t s) {
+    return residual ? launch_row_shape<WT, true>(p, rt, s) : launch_row_shape<WT, false>(p, rt, s);
+}
+
+template <typename WT>
+static int launch_bwd_small_wt(const BwdParams& p, const Route& rt, bool residual, hipStream_t s) {
+    return residual ? launch_small_shape<WT, true>(p, rt, s) : launch_small_shape<WT, false>(p, rt, s);
+}
+
+}  // namespace rmsn

@@ -1,0 +1,133 @@
+// dw reduce, zero fill, and the weight-dtype dispatch of the launchers.
+#include "rmsn_device.h"
+
+namespace rmsn {
+
+// Fixed-order reduction of P partial rows. A block owns 128 contiguous
+// bytes of columns (8 chunks of 16 bytes, so every partial row is read with
+// whole cache lines) and S = blockDim/8 slices: thread (chunk c, slice s)
+// sums partial rows s, s + S, s + 2S, ... in increasing order, four loads in
+// flight at a time. The slice sums are then added in a fixed order: a
+// butterfly over the 8 slices each wave holds, then the waves in index
+// order. Nothing depends on timing, so the result is bit-reproducible.
+template <typename PT>
+__global__ void __launch_bounds__(1024) k_dw_reduce(const PT* __restrict__ part, int64_t P,
+                                                    int32_t H, float* __restrict__ dw) {
+    constexpr int CPC = 16 / sizeof(PT);  // columns per 16-byte chunk
+    constexpr int CC = 8;                 // chunks per block
+    __shared__ double sm_red[16][CC * CPC];
+    const int S = blockDim.x / CC;
+    const int cc = threadIdx.x % CC;
+    const int s = threadIdx.x / CC;
+    const int64_t col0 = ((int64_t)blockIdx.x * CC + cc) * CPC;
+    const bool col_ok = col0 < H;
+    double a[CPC];
+#pragma unroll
+    for (int e = 0; e < CPC; ++e) a[e] = 0.0;
+    if (col_ok) {
+#pragma unroll 1
+        for (int64_t q = s; q < P; q += 4 * (int64_t)S) {
+            PT v[4][CPC];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int64_t row = q + (int64_t)u * S;
+#pragma unroll
+                for (int e = 0; e < CPC; ++e) v[u][e] = PT(0);
+                if (row < P) {
+                    const PT* src = part + row * H + col0;
+                    if constexpr (CPC == 2) {
+                        double2 t = *reinterpret_cast<const double2*>(src);
+                        v[u][0] = t.x;
+                        v[u][1] = t.y;
+                    } else {
+                        float4 t = *reinterpret_cast<const float4*>(src);
+                        v[u][0] = t.x;
+                        v[u][1] = t.y;
+                        v[u][2] = t.z;
+                        v[u][3] = t.w;
+                    }
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+#pragma unroll
+                for (int e = 0; e < CPC; ++e) a[e] += (double)v[u][e];
+        }
+    }
+    // butterfly over the wave's 8 slices (lane bits 3..5), fixed pairing
+#pragma unroll
+    for (int e = 0; e < CPC; ++e) {
+        a[e] += __shfl_xor(a[e], 8, 64);
+        a[e] += __shfl_xor(a[e], 16, 64);
+        a[e] += __shfl_xor(a[e], 32, 64);
+    }
+    const int wave = threadIdx.x >> 6;
+    const int nwaves = blockDim.x >> 6;
+    if ((threadIdx.x & 63) < CC) {
+#pragma unroll
+        for (int e = 0; e < CPC; ++e) sm_red[wave][cc * CPC + e] = a[e];
+    }
+    __syncthreads();
+    if (threadIdx.x < CC && col_ok) {
+#pragma unroll
+        for (int e = 0; e < CPC; ++e) {
+            double t = 0.0;
+            for (int w = 0; w < nwaves; ++w) t += sm_red[w][cc * CPC + e];
+            dw[col0 + e] = (float)t;
+        }
+    }
+}
+
+// Zero fill with vector stores (used for workspace initialisation; a kernel
+// rather than a memset so that it can sit inside captured graphs).
+__global__ void __launch_bounds__(256) k_fill_zero(uint4* p, int64_t n16, uint8_t* tail,
+                                                   int64_t ntail) {
+    const int64_t i0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t step = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = i0; i < n16; i += step) p[i] = make_uint4(0, 0, 0, 0);
+    if (i0 < ntail) tail[i0] = 0;
+}
+
+int launch_dw_reduce(const BwdParams& p, const Route& rt, hipStream_t s) {
+    const unsigned threads = (unsigned)rt.r.reduce_threads;
+    dim3 grid((unsigned)rt.r.reduce_grid), block(threads);
+    const size_t lds = 0;
+    if (rt.r.partial_f64)
+        hipLaunchKernelGGL(k_dw_reduce<double>, grid, block, lds, s,
+                           static_cast<const double*>(p.partial), (int64_t)rt.r.partials, p.H, p.dw);
+    else
+        hipLaunchKernelGGL(k_dw_reduce<float>, grid, block, lds, s,
+                           static_cast<const float*>(p.partial), (int64_t)rt.r.partials, p.H, p.dw);
+    return hipGetLastError() == hipSuccess ? RMSN_OK : RMSN_ERR_LAUNCH;
+}
+
+int launch_fill_zero(void* ptr, size_t bytes, hipStream_t s) {
+    if (bytes == 0) return RMSN_OK;
+    const int64_t n16 = (int64_t)(bytes / 16);
+    const int64_t ntail = (int64_t)(bytes % 16);
+    int64_t blocks = (n16 + 255) / 256;
+    if (blocks < 1) blocks = 1;
+    if (blocks > 4096) blocks = 4096;
+    hipLaunchKernelGGL(k_fill_zero, dim3((unsigned)blocks), dim3(256), 0, s,
+                       static_cast<uint4*>(ptr), n16, static_cast<uint8_t*>(ptr) + n16 * 16, ntail);
+    return hipGetLastError() == hipSuccess ? RMSN_OK : RMSN_ERR_LAUNCH;
+}
+
+int launch_fwd(const FwdParams& p, const Route& rt, rmsn_dtype_t wdt, bool residual,
+               hipStream_t s) {
+    return wdt == RMSN_BF16 ? launch_fwd_bf16w(p, rt, residual, s) : launch_fwd_f32w(p, rt, residual, s);
+}
+
+int launch_bwd_row(const BwdParams& p, const Route& rt, rmsn_dtype_t wdt, bool residual,
+                   hipStream_t s) {
+    return wdt == RMSN_BF16 ? launch_bwd_row_bf16w(p, rt, residual, s)
+                            : launch_bwd_row_f32w(p, rt, residual, s);
+}
+
+int launch_bwd_small(const BwdParams& p, const Route& rt, rmsn_dtype_t wdt, bool residual,
+                     hipStream_t s) {
+    return wdt == RMSN_BF16 ? launch_bwd_small_bf16w(p, rt, residual, s)
+                            : launch_bwd_small_f32w(p, rt, residual, s);
+}
+
+}  // namespace rmsn

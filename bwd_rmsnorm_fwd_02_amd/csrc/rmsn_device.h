@@ -74,6 +74,27 @@ __device__ __forceinline__ int64_t row_offset(int64_t r, int32_t heads, const Ro
     return (int64_t)t * a.st_t + (int64_t)hd * a.st_h;
 }
 
+// Make the compiler wait here for the loads that produced v. The memory
+// counter the compiler waits on is in-order and counts stores too, so a wait
+// for an older load also waits for every newer load or store. Forcing the
+// first tile of a software-pipelined loop to be complete before the loop
+// keeps the loop body free of such a wait, which would otherwise also drain
+// the next tile's prefetch at every iteration.
+__device__ __forceinline__ void use_now(const uint4& v) {
+    asm volatile("" ::"v"(v.x), "v"(v.y), "v"(v.z), "v"(v.w));
+}
+__device__ __forceinline__ void use_now(float v) { asm volatile("" ::"v"(v)); }
+
+// Workgroup barrier that orders LDS traffic only. A plain __syncthreads()
+// also waits for the wave's outstanding global loads and stores (the vector
+// memory counter covers both on gfx9-family parts), which would drain the
+// rows prefetched for the next iteration at every row.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // Butterfly sum over aligned groups of G lanes (G a power of two <= 64);
 // every lane of the group receives the group's sum. The pairing order is
 // fixed, so the result is bit-reproducible.

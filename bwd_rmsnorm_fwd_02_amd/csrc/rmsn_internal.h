@@ -70,6 +70,8 @@ struct Route {
 // Route table (route.cpp). op 0 fwd, 1 bwd.
 int route(int op, int64_t rows, int64_t H, rmsn_dtype_t wdt, int det, int residual,
           Route* out);
+// Tuning override of the route table (NULL clears).
+int set_route_knobs(int op, const rmsn_route_knobs_t* knobs);
 
 // Launchers (one per kernel file). They launch on `s` and return
 // hipGetLastError() mapped to an RMSN status.
@@ -81,6 +83,13 @@ int launch_dw_reduce(const BwdParams& p, const Route& rt, hipStream_t s);
 int launch_bwd_small(const BwdParams& p, const Route& rt, rmsn_dtype_t wdt, bool residual,
                      hipStream_t s);
 int launch_fill_zero(void* ptr, size_t bytes, hipStream_t s);
+// Per weight dtype (one translation unit each, compiled in parallel).
+int launch_fwd_bf16w(const FwdParams& p, const Route& rt, bool residual, hipStream_t s);
+int launch_fwd_f32w(const FwdParams& p, const Route& rt, bool residual, hipStream_t s);
+int launch_bwd_row_bf16w(const BwdParams& p, const Route& rt, bool residual, hipStream_t s);
+int launch_bwd_row_f32w(const BwdParams& p, const Route& rt, bool residual, hipStream_t s);
+int launch_bwd_small_bf16w(const BwdParams& p, const Route& rt, bool residual, hipStream_t s);
+int launch_bwd_small_f32w(const BwdParams& p, const Route& rt, bool residual, hipStream_t s);
 
 // Kernel timing hooks (api.cpp): bracket a launch when timing is enabled.
 void timer_begin(int kind, hipStream_t s);

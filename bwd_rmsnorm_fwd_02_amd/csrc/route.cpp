@@ -1,16 +1,17 @@
 // Route table: which kernel and launch shape serve (op, rows, H, weight
 // dtype, mode, form). Host-only and deterministic: a function of its
-// arguments alone (never of the device), so the deterministic backward's
-// row partition — and with it the dw bits — is fixed by the shape.
+// arguments (and of an explicit tuning override, if one is set), never of
+// the device, so the deterministic backward's row partition — and with it
+// the dw bits — is fixed by the shape.
 //
 // The pages pick among kernel kinds by windows of T per (GPU, H, weight
 // dtype) (flashinfer PR "fix(cake_rmsnorm): sm_100a and sm_107a dw-accuracy
 // backward routes", "Changed windows by reason"). The kinds kept here are
 // the ones that still hold on gfx950: a column-task kernel for small T
 // ("the fixed-claim column-task kernel runs T 1 to 64"), and a row kernel
-// with per-block dw partials plus a reduce (the "chunk-partials pair") or
-// with atomics for the non-deterministic mode. No dw-accuracy cut is needed
-// above that: FP64 dw accumulation keeps every shape inside the budget.
+// with per-block dw partials plus a reduce (the "chunk-partials pair"), or
+// with atomics. No dw-accuracy cut is needed above that: FP64 dw
+// accumulation keeps every shape inside the budget.
 #include <string.h>
 
 #include "rmsn_internal.h"
@@ -24,27 +25,126 @@ constexpr int64_t kSmallRows = 64;
 // Deterministic partials are stored in FP32 up to this many rows, FP64 above
 // (the FP32 rounding of each partial adds ~3e-8 * sqrt(T) absolute error).
 constexpr int64_t kPartialF32MaxRows = 8192;
-// Threads per CU the launch shapes aim to fill.
-constexpr int kThreadsPerCU = 2048;
-constexpr int kBwdThreadsPerCU = 1024;
 
-int ceil_div(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
+bool g_have_knobs[2] = {false, false};
+rmsn_route_knobs_t g_knobs[2];
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // Lanes per row for `nvec` 16-byte vectors at `nv` vectors per lane: a power
 // of two up to one wave, else a whole number of waves.
 int lanes_per_row(int nvec, int nv) {
-    const int need = ceil_div(nvec, nv);
+    const int need = (int)ceil_div(nvec, nv);
     if (need <= 64) {
         int t = 1;
         while (t < need) t <<= 1;
         return t;
     }
-    return ceil_div(need, 64) * 64;
+    return (int)ceil_div(need, 64) * 64;
 }
 
 size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
 
+// Default launch shapes of the row kernels by width (nvec 16-byte vectors
+// per row), chosen by timing every compiled shape on MI355X at the quoted
+// workloads: H 256 (per-head views), 2048, 4096 and 6144 (residual).
+// rpb_threads sets the row groups per block (threads / lanes per row).
+struct Shape {
+    int nv, unroll, rpb, bpc;
+};
+struct Entry {
+    int max_nvec, nv, unroll, rpb_threads, bpc;
+};
+constexpr Entry kFwdTable[] = {
+    {32, 4, 1, 256, 2},     // H <= 256: 8 lanes per row, 32 rows per block
+    {256, 2, 1, 512, 1},    // H <= 2048
+    {512, 4, 1, 512, 2},    // H <= 4096: 128 lanes per row
+    {1024, 2, 1, 0, 1},     // H <= 8192
+    {1 << 30, 4, 1, 0, 1},  // H <= 16384
+};
+constexpr Entry kBwdTable[] = {
+    {32, 1, 1, 256, 4},     // H <= 256
+    {256, 1, 2, 1024, 2},   // H <= 2048 (rows within one wave use <= 256 threads)
+    {1024, 1, 1, 0, 0},     // H <= 8192: one row per block, 2 blocks per CU at H 4096
+    {1 << 30, 2, 1, 0, 1},  // H <= 16384
+};
+
+template <size_t N>
+Shape lookup(const Entry (&t)[N], int nvec) {
+    for (const Entry& e : t) {
+        if (nvec <= e.max_nvec) {
+            Shape s{e.nv, e.unroll, 0, e.bpc};
+            const int need = (nvec + e.nv - 1) / e.nv;
+            int tpr = 1;
+            if (need <= 64) {
+                while (tpr < need) tpr <<= 1;
+            } else {
+                tpr = (need + 63) / 64 * 64;
+            }
+            int threads = e.rpb_threads;
+            if (tpr <= 64 && threads > 256) threads = 256;
+            if (threads > 0 && threads / tpr >= 1) s.rpb = threads / tpr;
+            return s;
+        }
+    }
+    return Shape{1, 1, 0, 0};
+}
+
+Shape default_fwd(int nvec) { return lookup(kFwdTable, nvec); }
+Shape default_bwd(int nvec) { return lookup(kBwdTable, nvec); }
+
+// Fill the row-kernel part of a route from a shape; 0 fields take defaults.
+// The checks mirror what the kernels are compiled for: (NV, U) pairs with
+// NV * U <= 8 (the backward NV <= 2), blocks of <= 256 threads when a row
+// fits in one wave, <= 512 when NV * U >= 4, else <= 1024.
+int row_shape(int op, int nvec, Shape sh, rmsn_route_t& r) {
+    const int nv = sh.nv;
+    if (!(nv == 1 || nv == 2 || (nv == 4 && op == 0))) return RMSN_ERR_SHAPE;
+    const int tpr = lanes_per_row(nvec, nv);
+    if (tpr > 1024) return RMSN_ERR_SHAPE;
+    const int u = sh.unroll;
+    if (!(u == 1 || u == 2 || u == 4 || u == 8)) return RMSN_ERR_SHAPE;
+    if (nv * u > 8) return RMSN_ERR_SHAPE;
+    int rpb = sh.rpb;
+    if (rpb <= 0) rpb = tpr <= 256 ? 256 / tpr : 1;
+    if ((int64_t)rpb * tpr > 1024) return RMSN_ERR_SHAPE;
+    const int threads = rpb * tpr;
+    if (threads % 64 != 0) return RMSN_ERR_SHAPE;
+    if (tpr <= 64 && threads > 256) return RMSN_ERR_SHAPE;
+    if (tpr > 64 && nv * u >= 4 && threads > 512) return RMSN_ERR_SHAPE;
+    r.vec_per_lane = nv;
+    r.lanes_per_row = tpr;
+    r.rows_per_block = rpb;
+    r.unroll = u;
+    r.block_threads = threads;
+    return RMSN_OK;
+}
+
+void apply_knobs(const rmsn_route_knobs_t& k, Shape& sh) {
+    if (k.vec_per_lane) sh.nv = k.vec_per_lane;
+    if (k.unroll) sh.unroll = k.unroll;
+    if (k.rows_per_block) sh.rpb = k.rows_per_block;
+    if (k.blocks_per_cu) sh.bpc = k.blocks_per_cu;
+}
+
 }  // namespace
+
+int set_route_knobs(int op, const rmsn_route_knobs_t* k) {
+    if (op != 0 && op != 1) return RMSN_ERR_SHAPE;
+    if (!k) {
+        g_have_knobs[op] = false;
+        return RMSN_OK;
+    }
+    if (k->blocks_per_cu < 0 || k->blocks_per_cu > 32 || k->rows_per_block < 0 ||
+        k->rows_per_block > 1024 || k->vec_per_lane < 0 || k->unroll < 0 || k->partial_f64 < 0 ||
+        k->partial_f64 > 2)
+        return RMSN_ERR_SHAPE;
+    if (k->kind != 0 && k->kind != RMSN_KIND_BWD_ROW_DET && k->kind != RMSN_KIND_BWD_ROW_ATOMIC)
+        return RMSN_ERR_SHAPE;
+    g_knobs[op] = *k;
+    g_have_knobs[op] = true;
+    return RMSN_OK;
+}
 
 int route(int op, int64_t rows, int64_t H, rmsn_dtype_t wdt, int det, int residual,
           Route* out) {
@@ -57,19 +157,16 @@ int route(int op, int64_t rows, int64_t H, rmsn_dtype_t wdt, int det, int residu
     (void)residual;
     const int nvec = (int)(H / kVec);
     rmsn_route_t& r = out->r;
+    int st;
 
     if (op == 0) {
-        // One-pass row forward; up to 1024 lanes per row.
-        const int nv = nvec <= 1024 ? 1 : 2;
-        const int tpr = lanes_per_row(nvec, nv);
-        const int rpb = tpr <= 256 ? 256 / tpr : 1;
+        Shape sh = default_fwd(nvec);
+        if (g_have_knobs[0]) apply_knobs(g_knobs[0], sh);
+        if ((st = row_shape(0, nvec, sh, r)) != RMSN_OK) return st;
         r.kind = RMSN_KIND_FWD_ROW;
-        r.vec_per_lane = nv;
-        r.lanes_per_row = tpr;
-        r.rows_per_block = rpb;
-        r.block_threads = tpr * rpb;
-        const int64_t cap = (int64_t)kPartitionCUs * (kThreadsPerCU / r.block_threads);
-        int64_t g = ceil_div(rows, rpb);
+        const int bpc = sh.bpc > 0 ? sh.bpc : (2048 / r.block_threads > 0 ? 2048 / r.block_threads : 1);
+        const int64_t cap = (int64_t)kPartitionCUs * bpc;
+        const int64_t g = ceil_div(rows, (int64_t)r.rows_per_block * r.unroll);
         r.grid = g < cap ? g : cap;
         if (r.grid < 1) r.grid = 1;
         return RMSN_OK;
@@ -86,8 +183,9 @@ int route(int op, int64_t rows, int64_t H, rmsn_dtype_t wdt, int det, int residu
         r.vec_per_lane = nv;
         r.lanes_per_row = tpr;
         r.rows_per_block = rpb;
+        r.unroll = 1;
         r.block_threads = 256;
-        const int ncol = ceil_div(nvec, vb);
+        const int64_t ncol = ceil_div(nvec, vb);
         r.grid = ncol + ceil_div(rows, rpb);
         r.partials = 0;
         r.reduce_grid = ncol;  // reported: blocks that run column tasks
@@ -96,29 +194,32 @@ int route(int op, int64_t rows, int64_t H, rmsn_dtype_t wdt, int det, int residu
     }
 
     // Large T: row kernel with register dw sums per block.
-    const int nv = nvec <= 1024 ? 1 : 2;
-    const int tpr = lanes_per_row(nvec, nv);
-    const int rpb = tpr <= 256 ? 256 / tpr : 1;
-    r.vec_per_lane = nv;
-    r.lanes_per_row = tpr;
-    r.rows_per_block = rpb;
-    r.block_threads = tpr * rpb;
-    // Every block must be resident at once (the partition is fixed, so a
-    // second round of blocks would double the tail): aim at 16 waves per CU.
-    int per_cu = kBwdThreadsPerCU / r.block_threads;
-    if (per_cu < 1) per_cu = 1;
-    const int64_t cap = (int64_t)kPartitionCUs * per_cu;
-    int64_t g = ceil_div(rows, 4 * rpb);  // at least ~4 rows per slot
+    Shape sh = default_bwd(nvec);
+    const rmsn_route_knobs_t* k = g_have_knobs[1] ? &g_knobs[1] : nullptr;
+    if (k) apply_knobs(*k, sh);
+    if ((st = row_shape(1, nvec, sh, r)) != RMSN_OK) return st;
+    // Every block should be resident at once (the partition is fixed, so a
+    // second round of blocks would lengthen the tail): by default 16 waves
+    // per CU.
+    int bpc = sh.bpc > 0 ? sh.bpc : 1024 / r.block_threads;
+    if (bpc < 1) bpc = 1;
+    const int64_t cap = (int64_t)kPartitionCUs * bpc;
+    const int64_t g = ceil_div(rows, 4LL * r.rows_per_block * r.unroll);  // >= ~4 iterations
     r.grid = g < cap ? g : cap;
     if (r.grid < 1) r.grid = 1;
-    if (det) {
+    int kind = det ? RMSN_KIND_BWD_ROW_DET : RMSN_KIND_BWD_ROW_DET;
+    if (k && k->kind && !det) kind = k->kind;
+    if (kind == RMSN_KIND_BWD_ROW_DET) {
         r.kind = RMSN_KIND_BWD_ROW_DET;
         r.partial_f64 = rows > kPartialF32MaxRows ? 1 : 0;
+        if (k && k->partial_f64) r.partial_f64 = k->partial_f64 == 1 ? 1 : 0;
         r.partials = r.grid;
-        const int cpc = r.partial_f64 ? 2 : 4;
-        r.reduce_grid = ceil_div(H, 16 * cpc);
-        out->workspace = align256((size_t)r.partials * (size_t)H * (r.partial_f64 ? 8 : 4));
+        const int psize = r.partial_f64 ? 8 : 4;
+        r.reduce_grid = ceil_div(H * psize, 128);
+        r.reduce_threads = 1024;  // 128 slices: one round of loads up to P = 512
+        out->workspace = align256((size_t)r.partials * (size_t)H * psize);
     } else {
+        if (r.vec_per_lane != 1 || r.unroll > 2) return RMSN_ERR_SHAPE;  // compiled variants
         r.kind = RMSN_KIND_BWD_ROW_ATOMIC;
         r.partial_f64 = 1;
         r.partials = 0;

@@ -26,23 +26,23 @@
  * - A view describes rows = T * heads rows of H contiguous elements; row
  *   (t, head) starts at t * stride_t + head * stride_h. rstd is always a
  *   contiguous FP32 array of T * heads values, index t * heads + head.
- * - Requirements: H a positive multiple of 8 and at most 16384; T, heads >= 0
- *   (rows == 0 is a no-op that returns RMSN_OK); BF16 tensor base pointers
- *   and strides 16-byte aligned (strides multiples of 8 elements); FP32
- *   weight/rstd/dw pointers 4-byte aligned; eps finite and >= 0.
+ * - Requirements: H a positive multiple of 8 and at most 16384; T >= 0 and
+ *   heads >= 1 (rows == T*heads == 0: the forward does nothing, the backward
+ *   writes dw = 0); rows < 2^31; BF16 tensor base pointers
+ *   and strides 16-byte aligned (strides multiples of 8 elements); weight
+ *   pointers 16-byte aligned; rstd/dw 4-byte aligned; eps finite and >= 0.
  * - Outputs are written in full (dw is overwritten, never accumulated into).
- *   An output may alias an input only exactly (same pointer, same view), for
- *   y/x in the forward and dx/dy in the backward; any other overlap of the
- *   byte spans of an output with another tensor is RMSN_ERR_ALIAS.
+ *   An output may alias an input only exactly (same pointer, same view), and
+ *   only in the forward: y over x, or h over x in the residual form. Any
+ *   other overlap of the byte spans of an output with another tensor, and
+ *   any output view whose rows overlap each other, is RMSN_ERR_ALIAS.
  * - Errors are returned as negative status codes before anything is
  *   enqueued (RMSN_ERR_LAUNCH is reported after a failed launch).
  *   rmsnorm_status_string() names them. Nothing is printed.
- * - Workspace: rmsnorm_bwd and rmsnorm_residual_bwd take a device workspace
- *   of at least rmsnorm_bwd_workspace_bytes(...) bytes, 256-byte aligned.
- *   For deterministic == 0 the workspace must be zero-filled before its
- *   first use (rmsnorm_workspace_init, or any zero fill); every completed
- *   non-deterministic call leaves it zero-filled again. Two calls that may
- *   run concurrently must not share a workspace.
+ * - Workspace: the backward entry points take a device workspace of at
+ *   least rmsnorm_bwd_workspace_bytes(...) bytes, 256-byte aligned, as
+ *   scratch: it needs no initialisation and its contents after a call are
+ *   unspecified. Two calls that may run concurrently must not share one.
  */
 #ifndef RMSNORM_MI355X_H
 #define RMSNORM_MI355X_H
@@ -107,7 +107,8 @@ int rmsnorm_residual_fwd(const void* x, const void* r, const void* w,
 size_t rmsnorm_bwd_workspace_bytes(int64_t rows, int64_t H, rmsn_dtype_t w_dtype,
                                    int deterministic);
 
-/* Zero-fill a workspace with a kernel on `stream` (safe inside graph capture). */
+/* Zero-fill a device buffer with a kernel on `stream` (no memset node, so it
+ * is safe inside graph capture). Not needed before the backward calls. */
 int rmsnorm_workspace_init(void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Plain backward on contiguous [T, H]. rstd is the forward's FP32 output.
@@ -156,12 +157,14 @@ typedef struct {
     int kind;            /* RMSN_KIND_* */
     int vec_per_lane;    /* 16-byte vectors each lane owns per row */
     int lanes_per_row;   /* threads that share one row */
-    int rows_per_block;  /* rows a block works on at once */
+    int rows_per_block;  /* row groups in a block */
+    int unroll;          /* rows a row group holds per iteration */
     int block_threads;
     int partial_f64;     /* dw partials in FP64 (1) or FP32 (0) */
+    int reduce_threads;  /* block size of the dw reduce kernel */
     int64_t grid;        /* blocks of the main kernel */
     int64_t partials;    /* dw partial rows written (0 if none) */
-    int64_t reduce_grid; /* blocks of the dw reduce kernel (0 if none) */
+    int64_t reduce_grid; /* blocks of the dw reduce (column-task blocks for small T) */
 } rmsn_route_t;
 
 /* The route table: which kernel and launch shape serve this problem.
@@ -169,6 +172,23 @@ typedef struct {
  * Returns RMSN_OK or RMSN_ERR_SHAPE / RMSN_ERR_DTYPE / RMSN_ERR_NULL. */
 int rmsnorm_route_query(int op, int64_t rows, int64_t H, rmsn_dtype_t w_dtype,
                         int deterministic, int residual, rmsn_route_t* out);
+
+/* Launch-shape knobs for benchmarks and tuning sweeps (not part of the
+ * method). A zero field keeps the table's choice. The route is still derived
+ * and checked by the same code, so a knob the kernels cannot honour makes
+ * the next call of that op fail with RMSN_ERR_SHAPE instead of launching.
+ * Overriding the backward changes the deterministic partition, hence the dw
+ * bits (they stay reproducible for a fixed setting). The small-T column-task
+ * route is not affected. Process-wide; NULL clears. */
+typedef struct {
+    int vec_per_lane;   /* 1, 2 or 4 (backward: 1 or 2) */
+    int unroll;         /* 1, 2 or 4; only 1 when a row spans several waves */
+    int rows_per_block; /* row groups per block; block size <= 1024 */
+    int blocks_per_cu;  /* grid cap = 256 * blocks_per_cu */
+    int partial_f64;    /* backward: 1 FP64 partials, 2 FP32 partials */
+    int kind;           /* backward: RMSN_KIND_BWD_ROW_DET or RMSN_KIND_BWD_ROW_ATOMIC */
+} rmsn_route_knobs_t;
+int rmsnorm_route_override(int op, const rmsn_route_knobs_t* knobs);
 
 /* Per-kernel timing with HIP events on the caller's stream (for benchmarks).
  * While enabled, every kernel the library launches is bracketed by two

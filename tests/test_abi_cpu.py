@@ -134,7 +134,9 @@ def test_route_small_t_uses_column_tasks_in_both_modes():
             st, r = route(1, rows, 256, 1, det)
             assert st == 0 and r.kind == _lib.RMSN_KIND_BWD_COLTASK
         st, r = route(1, 65, 256, 1, det)
-        assert r.kind == (_lib.RMSN_KIND_BWD_ROW_DET if det else _lib.RMSN_KIND_BWD_ROW_ATOMIC)
+        # above the column-task window both modes run the two-stage path by
+        # default (the atomic finalise measured slower on MI355X)
+        assert r.kind == _lib.RMSN_KIND_BWD_ROW_DET
     assert lib.rmsnorm_bwd_workspace_bytes(64, 256, 1, 1) == 0
 
 
@@ -144,7 +146,8 @@ def test_route_deterministic_partition_is_a_function_of_shape():
         _, a = route(1, rows, H, 0, 1, 0)
         _, b = route(1, rows, H, 1, 1, 1)
         assert a.grid == b.grid and a.partials == a.grid and a.kind == _lib.RMSN_KIND_BWD_ROW_DET
-        assert 1 <= a.grid <= 256 * 1024 // a.block_threads
+        # every block owns at least one full iteration of rows
+        assert 1 <= a.grid and a.grid * a.rows_per_block * a.unroll <= rows
         ws = lib.rmsnorm_bwd_workspace_bytes(rows, H, 0, 1)
         assert ws >= a.partials * H * (8 if a.partial_f64 else 4)
         assert a.reduce_grid * 16 * (2 if a.partial_f64 else 4) >= H
@@ -173,7 +176,34 @@ def test_route_rejects_bad_shapes():
     assert route(2, 10, 64)[0] == -3
 
 
-def test_route_nondeterministic_uses_atomic_finalise():
-    st, r = route(1, 131072, 2048, 1, 0)
-    assert st == 0 and r.kind == _lib.RMSN_KIND_BWD_ROW_ATOMIC and r.partials == 0
-    assert lib.rmsnorm_bwd_workspace_bytes(131072, 2048, 1, 0) >= 2048 * 8 + 4
+def test_route_override_selects_atomic_and_rejects_bad_knobs():
+    K = _lib.RouteKnobs
+    try:
+        assert lib.rmsnorm_route_override(1, ctypes.byref(K(0, 0, 0, 0, 0, _lib.RMSN_KIND_BWD_ROW_ATOMIC))) == 0
+        st, r = route(1, 131072, 2048, 1, 0)
+        assert st == 0 and r.kind == _lib.RMSN_KIND_BWD_ROW_ATOMIC and r.partials == 0
+        st, r = route(1, 131072, 2048, 1, 1)  # deterministic calls ignore the kind knob
+        assert st == 0 and r.kind == _lib.RMSN_KIND_BWD_ROW_DET
+        assert lib.rmsnorm_bwd_workspace_bytes(131072, 2048, 1, 0) >= 2048 * 8 + 4
+        # knobs the kernels cannot honour make the route fail (no launch)
+        assert lib.rmsnorm_route_override(1, ctypes.byref(K(3, 0, 0, 0, 0, 0))) == 0
+        assert route(1, 131072, 2048, 1, 1)[0] == -3
+        assert lib.rmsnorm_route_override(1, ctypes.byref(K(2, 8, 0, 0, 0, 0))) == 0
+        assert route(1, 4096, 4096, 0, 1)[0] == -3     # NV * U > 8 is not compiled
+        assert lib.rmsnorm_route_override(1, ctypes.byref(K(1, 8, 2, 0, 0, 0))) == 0
+        assert route(1, 4096, 4096, 0, 1)[0] == -3     # 1024 threads with NV * U >= 4
+        assert lib.rmsnorm_route_override(1, ctypes.byref(K(2, 4, 0, 0, 0, 3))) == 0
+        assert route(1, 4096, 4096, 0, 0)[0] == -3     # atomic variant compiled for NV 1, U <= 2
+        assert lib.rmsnorm_route_override(1, ctypes.byref(K(1, 0, 64, 0, 0, 0))) == 0
+        assert route(1, 4096, 256, 0, 1)[0] == -3      # 64 x 32 lanes > 256 threads
+        assert lib.rmsnorm_route_override(1, ctypes.byref(K(0, 0, 0, 99, 0, 0))) == -3
+        assert lib.rmsnorm_route_override(0, ctypes.byref(K(4, 4, 0, 0, 0, 0))) == 0
+        assert route(0, 4096, 4096)[0] == -3
+        assert lib.rmsnorm_route_override(0, ctypes.byref(K(1, 4, 0, 0, 0, 0))) == 0
+        st, r = route(0, 4096, 256)
+        assert st == 0 and r.unroll == 4 and r.vec_per_lane == 1
+    finally:
+        lib.rmsnorm_route_override(0, None)
+        lib.rmsnorm_route_override(1, None)
+    st, r = route(0, 4096, 256)
+    assert st == 0 and r.unroll == 2

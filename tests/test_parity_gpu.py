@@ -190,23 +190,25 @@ def test_zero_rows_and_errors():
         rn.rmsnorm_fwd(xx, w, eps=-1.0)
 
 
-def test_nondet_workspace_left_zeroed():
+def test_atomic_route_with_dirty_workspace():
+    """The atomic route clears its own accumulator: a workspace full of
+    garbage (as the two-stage route leaves it) gives the same budget."""
     wl = synth.make(T=4096, H=1024, w_dtype="bf16", seed=5)
     _, r32 = oracle_rstd32(wl.x, wl.w.f64, wl.eps)
-    need = rn.rmsnorm_bwd_workspace_bytes(4096, 1024, torch.bfloat16, False)
-    ws = torch.zeros(need + 256, dtype=torch.uint8, device=DEV)
-    off = (-ws.data_ptr()) % 256
-    ws = ws[off:off + need]
-    dws = []
-    for _ in range(3):
-        _, dw = rn.rmsnorm_bwd(dev_bf16(wl.dy), dev_bf16(wl.x), dev_f32(r32), dev_w(wl.w),
-                               deterministic=False, workspace=ws)
-        torch.cuda.synchronize()
-        assert int(ws.count_nonzero()) == 0
-        dws.append(dw.cpu().numpy())
     _, _, dw64 = oracle.bwd(wl.dy, wl.x, r32.astype(np.float64), wl.w.f64, want_dx=False)
-    for d in dws:
-        check_dw("dw non-det", d, dw64)
+    try:
+        rn.rmsnorm_route_override("bwd", kind=3)
+        need = rn.rmsnorm_bwd_workspace_bytes(4096, 1024, torch.bfloat16, False)
+        ws = torch.full((need + 256,), 0x5A, dtype=torch.uint8, device=DEV)
+        ws = ws[(-ws.data_ptr()) % 256:]
+        for _ in range(3):
+            _, dw = rn.rmsnorm_bwd(dev_bf16(wl.dy), dev_bf16(wl.x), dev_f32(r32), dev_w(wl.w),
+                                   deterministic=False, workspace=ws)
+            torch.cuda.synchronize()
+            check_dw("dw non-det atomic", dw.cpu().numpy(), dw64)
+            ws.fill_(0x5A)
+    finally:
+        rn.rmsnorm_route_override("bwd")
 
 
 # --------------------------------------------------------- full-size cases
@@ -317,3 +319,61 @@ def test_full_size_config(name):
     for i in range(3):
         _, dwn = run_bwd(False)
         check_dw(f"dw non-det run {i}", dwn, dw64)
+
+
+# ------------------------------------------------- non-default launch shapes
+
+VARIANTS = [
+    # (T, H, w dtype, op, knobs)
+    (3000, 256, "f32", "fwd", dict(vec_per_lane=1, unroll=4)),
+    (3000, 256, "f32", "fwd", dict(vec_per_lane=1, unroll=1, rows_per_block=2)),
+    (777, 2048, "bf16", "fwd", dict(vec_per_lane=4, unroll=1)),
+    (777, 4096, "bf16", "fwd", dict(vec_per_lane=4)),
+    (777, 4096, "f32", "fwd", dict(vec_per_lane=1, rows_per_block=2, blocks_per_cu=1)),
+    (3000, 256, "f32", "bwd", dict(vec_per_lane=1, unroll=4, blocks_per_cu=2)),
+    (3000, 256, "bf16", "bwd", dict(vec_per_lane=1, unroll=1, rows_per_block=4)),
+    (777, 2048, "f32", "bwd", dict(vec_per_lane=2, rows_per_block=2, partial_f64=1)),
+    (777, 4096, "bf16", "bwd", dict(vec_per_lane=2, blocks_per_cu=2, partial_f64=2)),
+    (5000, 6144, "bf16", "bwd", dict(vec_per_lane=1, blocks_per_cu=2)),
+    (777, 4096, "bf16", "fwd", dict(vec_per_lane=1, unroll=8)),
+    (777, 6144, "bf16", "fwd", dict(vec_per_lane=2, unroll=4)),
+    (777, 4096, "bf16", "bwd", dict(vec_per_lane=1, unroll=8)),
+    (5000, 2048, "f32", "bwd", dict(vec_per_lane=1, unroll=4, rows_per_block=2)),
+    (1000, 6144, "bf16", "bwd", dict(vec_per_lane=2, unroll=2)),
+    (2500, 1024, "f32", "bwd", dict(kind=3)),  # atomic finalise, non-deterministic calls
+    (300, 256, "f32", "bwd", dict(kind=3, unroll=2)),
+]
+
+
+@pytest.mark.parametrize("T,H,wdt,op,knobs", VARIANTS)
+def test_route_variants(T, H, wdt, op, knobs):
+    _announce(f"variant {op} T={T} H={H} w={wdt} {knobs}")
+    wl = synth.make(T=T, H=H, w_dtype=wdt, seed=T + H + 1)
+    try:
+        rn.rmsnorm_route_override(op, **knobs)
+        if op == "fwd":
+            y, rstd = rn.rmsnorm_fwd(dev_bf16(wl.x), dev_w(wl.w), wl.eps)
+            torch.cuda.synchronize()
+            r64, y64 = oracle.fwd(wl.x, wl.w.f64, wl.eps)
+            check_rstd("rstd", rstd.cpu().numpy(), r64)
+            check_bf16_strict("y", host_bits(y), y64)
+            return
+        _, r32 = oracle_rstd32(wl.x, wl.w.f64, wl.eps)
+        r32_64 = r32.astype(np.float64)
+        dx64, c64, dw64 = oracle.bwd(wl.dy, wl.x, r32_64, wl.w.f64)
+        E = dx_bound(to_f64(wl.x), to_f64(wl.dy), wl.w.f64, r32_64, c64, H)
+        det = "kind" not in knobs
+        outs = []
+        for _ in range(3):
+            dx, dw = _bwd_case(wl, det, r32)
+            check_dx("dx", dx, dx64, E)
+            check_dw("dw", dw, dw64)
+            outs.append((dx, dw))
+        if det:
+            assert all(np.array_equal(o[1].view(np.uint32), outs[0][1].view(np.uint32)) for o in outs)
+        else:
+            # same row layout, deterministic mode: dx bit-identical
+            dx_det, _ = _bwd_case(wl, True, r32)
+            assert np.array_equal(outs[0][0], dx_det)
+    finally:
+        rn.rmsnorm_route_override(op)
