@@ -178,6 +178,7 @@ def test_route_rejects_bad_shapes():
 
 def test_route_override_selects_atomic_and_rejects_bad_knobs():
     K = _lib.RouteKnobs
+    _, before = route(0, 4096, 256)
     try:
         assert lib.rmsnorm_route_override(1, ctypes.byref(K(0, 0, 0, 0, 0, _lib.RMSN_KIND_BWD_ROW_ATOMIC))) == 0
         st, r = route(1, 131072, 2048, 1, 0)
@@ -206,4 +207,4 @@ def test_route_override_selects_atomic_and_rejects_bad_knobs():
         lib.rmsnorm_route_override(0, None)
         lib.rmsnorm_route_override(1, None)
     st, r = route(0, 4096, 256)
-    assert st == 0 and r.unroll == 2
+    assert st == 0 and (r.unroll, r.vec_per_lane, r.grid) == (before.unroll, before.vec_per_lane, before.grid)
