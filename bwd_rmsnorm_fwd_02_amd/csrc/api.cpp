@@ -104,18 +104,20 @@ constexpr size_t kTimerPool = 4096;
 
 namespace rmsn {
 
-void timer_begin(int kind, hipStream_t s) {
-    if (!g_timer.enabled || g_timer.used >= g_timer.start.size()) return;
-    g_timer.pending_kind = kind;
-    (void)hipEventRecord(g_timer.start[g_timer.used], s);
+void timer_begin(int kind, hipStream_t) {
+    g_timer.pending_kind = g_timer.enabled ? kind : -1;
 }
 
-void timer_end(int kind, hipStream_t s) {
-    if (!g_timer.enabled || g_timer.used >= g_timer.start.size() || g_timer.pending_kind != kind) return;
-    (void)hipEventRecord(g_timer.stop[g_timer.used], s);
-    g_timer.kind[g_timer.used] = kind;
+void timer_end(int, hipStream_t) { g_timer.pending_kind = -1; }
+
+bool timer_take(hipEvent_t* start, hipEvent_t* stop) {
+    if (!g_timer.enabled || g_timer.pending_kind < 0 || g_timer.used >= g_timer.start.size()) return false;
+    *start = g_timer.start[g_timer.used];
+    *stop = g_timer.stop[g_timer.used];
+    g_timer.kind[g_timer.used] = g_timer.pending_kind;
     g_timer.used++;
     g_timer.pending_kind = -1;
+    return true;
 }
 
 }  // namespace rmsn

@@ -423,13 +423,13 @@ static int launch_row_mode(const BwdParams& p, const Route& rt, size_t lds, hipS
     dim3 grid((unsigned)rt.r.grid), block((unsigned)rt.r.block_threads);
     if (rt.r.kind == RMSN_KIND_BWD_ROW_ATOMIC) {
         if constexpr (NV == 1 && U <= 2)
-            hipLaunchKernelGGL((k_bwd_row<NV, U, WT, RES, WIDE, kModeAtomic>), grid, block, lds, s, p);
+            launch_kernel((k_bwd_row<NV, U, WT, RES, WIDE, kModeAtomic>), grid, block, lds, s, p);
         else
             return RMSN_ERR_SHAPE;
     } else if (rt.r.partial_f64) {
-        hipLaunchKernelGGL((k_bwd_row<NV, U, WT, RES, WIDE, kModePartF64>), grid, block, lds, s, p);
+        launch_kernel((k_bwd_row<NV, U, WT, RES, WIDE, kModePartF64>), grid, block, lds, s, p);
     } else {
-        hipLaunchKernelGGL((k_bwd_row<NV, U, WT, RES, WIDE, kModePartF32>), grid, block, lds, s, p);
+        launch_kernel((k_bwd_row<NV, U, WT, RES, WIDE, kModePartF32>), grid, block, lds, s, p);
     }
     return hipGetLastError() == hipSuccess ? RMSN_OK : RMSN_ERR_LAUNCH;
 }
@@ -470,7 +470,7 @@ static int launch_small_t(const BwdParams& p, const Route& rt, hipStream_t s) {
     const size_t lds_red =
         sizeof(float) * 2 * r.rows_per_block * (r.lanes_per_row > 64 ? r.lanes_per_row / 64 : 1);
     if (lds_red > lds) lds = lds_red;
-    hipLaunchKernelGGL((k_bwd_small<NV, WT, RES>), dim3((unsigned)r.grid), dim3(256), lds, s, p);
+    launch_kernel((k_bwd_small<NV, WT, RES>), dim3((unsigned)r.grid), dim3(256), lds, s, p);
     return hipGetLastError() == hipSuccess ? RMSN_OK : RMSN_ERR_LAUNCH;
 }
 

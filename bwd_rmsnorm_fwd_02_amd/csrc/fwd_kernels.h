@@ -207,9 +207,9 @@ static int launch_fwd_t(const FwdParams& p, const Route& rt, hipStream_t s) {
     const size_t lds = fwd_lds_bytes(r);
     dim3 grid((unsigned)r.grid), block((unsigned)r.block_threads);
     if (r.lanes_per_row > 64)
-        hipLaunchKernelGGL((k_fwd<NV, U, WT, RES, true>), grid, block, lds, s, p);
+        launch_kernel((k_fwd<NV, U, WT, RES, true>), grid, block, lds, s, p);
     else
-        hipLaunchKernelGGL((k_fwd<NV, U, WT, RES, false>), grid, block, lds, s, p);
+        launch_kernel((k_fwd<NV, U, WT, RES, false>), grid, block, lds, s, p);
     return hipGetLastError() == hipSuccess ? RMSN_OK : RMSN_ERR_LAUNCH;
 }
 

@@ -93,10 +93,10 @@ int launch_dw_reduce(const BwdParams& p, const Route& rt, hipStream_t s) {
     dim3 grid((unsigned)rt.r.reduce_grid), block(threads);
     const size_t lds = 0;
     if (rt.r.partial_f64)
-        hipLaunchKernelGGL(k_dw_reduce<double>, grid, block, lds, s,
+        launch_kernel(k_dw_reduce<double>, grid, block, lds, s,
                            static_cast<const double*>(p.partial), (int64_t)rt.r.partials, p.H, p.dw);
     else
-        hipLaunchKernelGGL(k_dw_reduce<float>, grid, block, lds, s,
+        launch_kernel(k_dw_reduce<float>, grid, block, lds, s,
                            static_cast<const float*>(p.partial), (int64_t)rt.r.partials, p.H, p.dw);
     return hipGetLastError() == hipSuccess ? RMSN_OK : RMSN_ERR_LAUNCH;
 }
@@ -108,7 +108,7 @@ int launch_fill_zero(void* ptr, size_t bytes, hipStream_t s) {
     int64_t blocks = (n16 + 255) / 256;
     if (blocks < 1) blocks = 1;
     if (blocks > 4096) blocks = 4096;
-    hipLaunchKernelGGL(k_fill_zero, dim3((unsigned)blocks), dim3(256), 0, s,
+    launch_kernel(k_fill_zero, dim3((unsigned)blocks), dim3(256), 0, s,
                        static_cast<uint4*>(ptr), n16, static_cast<uint8_t*>(ptr) + n16 * 16, ntail);
     return hipGetLastError() == hipSuccess ? RMSN_OK : RMSN_ERR_LAUNCH;
 }

@@ -3,6 +3,7 @@
 // the launcher entry points each kernel file provides.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -91,8 +92,20 @@ int launch_bwd_row_f32w(const BwdParams& p, const Route& rt, bool residual, hipS
 int launch_bwd_small_bf16w(const BwdParams& p, const Route& rt, bool residual, hipStream_t s);
 int launch_bwd_small_f32w(const BwdParams& p, const Route& rt, bool residual, hipStream_t s);
 
-// Kernel timing hooks (api.cpp): bracket a launch when timing is enabled.
+// Kernel timing hooks (api.cpp). timer_begin names the kernel kind the API
+// is about to launch; when timing is enabled, the next launch takes a pair
+// of events that the dispatch itself records (no separate marker packets).
 void timer_begin(int kind, hipStream_t s);
 void timer_end(int kind, hipStream_t s);
+bool timer_take(hipEvent_t* start, hipEvent_t* stop);
+
+template <typename K, typename... Args>
+inline void launch_kernel(K kernel, dim3 grid, dim3 block, size_t lds, hipStream_t s, Args... args) {
+    hipEvent_t e0 = nullptr, e1 = nullptr;
+    if (timer_take(&e0, &e1))
+        hipExtLaunchKernelGGL(kernel, grid, block, (uint32_t)lds, s, e0, e1, 0u, args...);
+    else
+        hipLaunchKernelGGL(kernel, grid, block, lds, s, args...);
+}
 
 }  // namespace rmsn
