@@ -18,11 +18,11 @@
 // plus periodic FP64 fold) that the pages use on hardware with slow FP64.
 //
 // How the per-block sums meet (the only difference between the modes):
-// * deterministic: block b owns the contiguous row range
-//   [b*rows/P, (b+1)*rows/P), where P (the grid) is a function of the shape
-//   only; row slots inside the block are combined in slot order; the block
-//   writes its partial row; k_dw_reduce then sums the P partials in a fixed
-//   order. No step depends on scheduling or on the CU count.
+// * deterministic: block b takes the row tiles b, b + P, b + 2P, ..., where
+//   P (the grid) is a function of the shape only; it adds them in that order,
+//   combines its row slots in slot order and writes its partial row;
+//   k_dw_reduce then sums the P partials in a fixed order. No step depends
+//   on scheduling or on the CU count.
 // * atomic (non-deterministic): the same blocks add their sums into an FP64
 //   accumulator with hardware atomics; the last block to finish (a ticket
 //   counter) converts it to FP32 dw.
@@ -202,7 +202,7 @@ __device__ __forceinline__ void bwd_store(const BwdParams& p, int64_t r0, int64_
 #pragma unroll
         for (int v = 0; v < NV; ++v) {
             if (!vok[v]) continue;
-            st16(p.dx + odx + (int64_t)(lr + v * p.tpr) * kVec, out[k][v]);
+            st16_stream(p.dx + odx + (int64_t)(lr + v * p.tpr) * kVec, out[k][v]);
         }
     }
 }
@@ -224,9 +224,8 @@ __device__ __forceinline__ void load_weights(const BwdParams& p, int slot, int l
 }
 
 // Large-T row kernel: dx for the block's rows plus the block's dw sums.
-// Block b owns rows [b*rows/P, (b+1)*rows/P); each iteration a row group
-// takes U rows of it. With U <= 2 the next iteration's rows are loaded
-// before the current ones are processed.
+// Each iteration a row group takes U rows; with U <= 2 the next iteration's
+// rows are loaded before the current ones are processed.
 template <int NV, int U, typename WT, bool RES, bool WIDE, int MODE>
 __global__ void __launch_bounds__(WIDE ? (NV * U >= 4 ? 512 : 1024) : 256) k_bwd_row(BwdParams p) {
     constexpr bool PF = U <= 2;
@@ -248,22 +247,25 @@ __global__ void __launch_bounds__(WIDE ? (NV * U >= 4 ? 512 : 1024) : 256) k_bwd
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc[v][e] = 0.0;
 
+    // Block b takes iterations b, b + P, b + 2P, ... of per_iter rows each:
+    // a fixed partition (a function of the shape and the route only) in which
+    // all blocks sweep one compact window of rows together, which keeps the
+    // HBM access stream local.
     const int64_t P = gridDim.x;
     const int64_t b = blockIdx.x;
-    const int64_t rbeg = (b * p.rows) / P;
-    const int64_t rend = ((b + 1) * p.rows) / P;
     const int64_t per_iter = (int64_t)p.rpb * U;
-    const int64_t nit = (rend - rbeg + per_iter - 1) / per_iter;
+    const int64_t stride = P * per_iter;
+    const int64_t rend = p.rows;
     int buf = 0;
-    if (nit > 0) {
+    int64_t r0 = b * per_iter;
+    if (r0 < rend) {
         BwdTile<NV, U, RES> cur;
         BwdTile<NV, PF ? U : 1, RES> nxt;
-        bwd_load<NV, U, RES>(p, rbeg, rend, slot, lr, cur);
+        bwd_load<NV, U, RES>(p, r0, rend, slot, lr, cur);
         bwd_ready<NV, U, RES>(cur);
 #pragma unroll 1
-        for (int64_t it = 0; it < nit; ++it) {
-            const int64_t r0 = rbeg + it * per_iter;
-            if constexpr (PF) bwd_load<NV, U, RES>(p, r0 + per_iter, rend, slot, lr, nxt);
+        for (; r0 < rend; r0 += stride) {
+            if constexpr (PF) bwd_load<NV, U, RES>(p, r0 + stride, rend, slot, lr, nxt);
             uint4 out[U][NV];
             bwd_compute<NV, U, RES, WIDE, true>(p, r0, rend, slot, lr, wv, vok, cur, acc, out, red, buf);
             // The next tile must be complete before its registers take over;
@@ -274,7 +276,7 @@ __global__ void __launch_bounds__(WIDE ? (NV * U >= 4 ? 512 : 1024) : 256) k_bwd
             }
             bwd_store<NV, U>(p, r0, rend, slot, lr, vok, out);
             if constexpr (!PF) {
-                if (it + 1 < nit) bwd_load<NV, U, RES>(p, r0 + per_iter, rend, slot, lr, cur);
+                if (r0 + stride < rend) bwd_load<NV, U, RES>(p, r0 + stride, rend, slot, lr, cur);
             }
         }
     }

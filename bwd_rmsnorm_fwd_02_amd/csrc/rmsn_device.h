@@ -46,6 +46,16 @@ __device__ __forceinline__ void st16(uint16_t* p, const uint4& v) {
     *reinterpret_cast<uint4*>(p) = v;
 }
 
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// Streaming store for outputs nothing in the op reads back (y, dx): marked
+// non-temporal so they do not displace inputs that are read again soon
+// (x is read by the forward and again by the backward) from the caches.
+__device__ __forceinline__ void st16_stream(uint16_t* p, const uint4& v) {
+    u32x4 w = {v.x, v.y, v.z, v.w};
+    __builtin_nontemporal_store(w, reinterpret_cast<u32x4*>(p));
+}
+
 // Weight vector of 8 elements as FP32 (BF16 widened exactly).
 template <typename WT>
 __device__ __forceinline__ void load_w8(const void* w, int v, float (&f)[8]);

@@ -58,14 +58,15 @@ struct Entry {
 constexpr Entry kFwdTable[] = {
     {32, 4, 1, 256, 2},     // H <= 256: 8 lanes per row, 32 rows per block
     {256, 2, 1, 512, 1},    // H <= 2048
-    {512, 4, 1, 512, 2},    // H <= 4096: 128 lanes per row
+    {512, 2, 4, 256, 4},    // H <= 4096: 256 lanes per row, 4 rows per iteration
     {1024, 2, 1, 0, 1},     // H <= 8192
     {1 << 30, 4, 1, 0, 1},  // H <= 16384
 };
 constexpr Entry kBwdTable[] = {
-    {32, 1, 1, 256, 4},     // H <= 256
-    {256, 1, 2, 1024, 2},   // H <= 2048 (rows within one wave use <= 256 threads)
-    {1024, 1, 1, 0, 0},     // H <= 8192: one row per block, 2 blocks per CU at H 4096
+    {32, 2, 1, 128, 4},     // H <= 256: 16 lanes per row, 8 rows per block, 4 blocks per CU
+    {256, 1, 2, 512, 1},    // H <= 2048: 2 row groups of up to 256 lanes, 1 block per CU
+    {512, 1, 1, 0, 2},      // H <= 4096: one row per block, 2 blocks per CU
+    {1024, 2, 2, 0, 1},     // H <= 8192
     {1 << 30, 2, 1, 0, 1},  // H <= 16384
 };
 
@@ -207,7 +208,7 @@ int route(int op, int64_t rows, int64_t H, rmsn_dtype_t wdt, int det, int residu
     int bpc = sh.bpc > 0 ? sh.bpc : 1024 / r.block_threads;
     if (bpc < 1) bpc = 1;
     const int64_t cap = (int64_t)kPartitionCUs * bpc;
-    const int64_t g = ceil_div(rows, 4LL * r.rows_per_block * r.unroll);  // >= ~4 iterations
+    const int64_t g = ceil_div(rows, 4LL * r.rows_per_block * r.unroll);  // ~4 iterations or more
     r.grid = g < cap ? g : cap;
     if (r.grid < 1) r.grid = 1;
     int kind = det ? RMSN_KIND_BWD_ROW_DET : RMSN_KIND_BWD_ROW_DET;

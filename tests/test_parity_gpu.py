@@ -341,7 +341,7 @@ VARIANTS = [
     (5000, 2048, "f32", "bwd", dict(vec_per_lane=1, unroll=4, rows_per_block=2)),
     (1000, 6144, "bf16", "bwd", dict(vec_per_lane=2, unroll=2)),
     (2500, 1024, "f32", "bwd", dict(kind=3)),  # atomic finalise, non-deterministic calls
-    (300, 256, "f32", "bwd", dict(kind=3, unroll=2)),
+    (300, 256, "f32", "bwd", dict(kind=3, vec_per_lane=1, unroll=2)),
 ]
 
 
