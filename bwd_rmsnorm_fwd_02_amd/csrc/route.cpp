@@ -123,8 +123,11 @@ int row_shape(int op, int nvec, Shape sh, rmsn_route_t& r) {
 
 void apply_knobs(const rmsn_route_knobs_t& k, Shape& sh) {
     if (k.vec_per_lane && k.vec_per_lane != sh.nv) {
+        // the table's rows per iteration and row groups per block were sized
+        // for its own vector width
         sh.nv = k.vec_per_lane;
-        sh.rpb = 0;  // the table's row groups per block were sized for its own width
+        sh.unroll = 1;
+        sh.rpb = 0;
     }
     if (k.unroll) sh.unroll = k.unroll;
     if (k.rows_per_block) sh.rpb = k.rows_per_block;
