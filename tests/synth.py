@@ -102,9 +102,10 @@ class Workload:
 
 def make(T: int, H: int, w_dtype: str, seed: int, *, heads: int = 1,
          residual: bool = False, with_dres: bool = True, heavy_frac: float = 0.0,
-         strided_row: int = 0, name: str = "") -> Workload:
+         strided_row: int = 0, same_sign: bool = False, name: str = "") -> Workload:
     """Build a workload. ``strided_row`` > 0 selects the strided per-head form:
-    x lives in a ``[T, strided_row]`` buffer with head stride H."""
+    x lives in a ``[T, strided_row]`` buffer with head stride H. ``same_sign``
+    takes |x| and |dy| (every dy*xhat term positive, so dw grows like T)."""
     rng = np.random.default_rng(seed)
     w = weight(rng, H, w_dtype)
     rows = T * heads
@@ -126,11 +127,22 @@ def make(T: int, H: int, w_dtype: str, seed: int, *, heads: int = 1,
         x = bf16_bits(xf)
     r = normal_bf16(rng, (rows, H)) if residual else None
     dy = normal_bf16(rng, (rows, H))
+    if same_sign:
+        x = x & np.uint16(0x7FFF)   # clear the BF16 sign bit: |x|
+        dy = dy & np.uint16(0x7FFF)
     dres = normal_bf16(rng, (rows, H)) if (residual and with_dres) else None
     return Workload(name=name, T=T, heads=heads, H=H, w=w, x=x, dy=dy, r=r,
                     dres=dres, xbuf=xbuf, x_stride_t=st_t, x_stride_h=st_h,
                     heavy_rows=heavy)
 
+
+# Input families for accuracy sweeps (the pages use three families; their
+# definitions are not given, so these are this library's choice).
+FAMILIES = {
+    "normal": dict(),
+    "heavy_rows": dict(heavy_frac=0.01),
+    "same_sign": dict(same_sign=True),
+}
 
 # The five workloads the method is quoted on (T, H, weight dtype, form).
 CONFIGS = {

@@ -1,0 +1,80 @@
+"""dw accuracy sweep (flashinfer PR "fix(cake_rmsnorm): sm_100a and sm_107a
+dw-accuracy backward routes", section "Changed windows by reason", and the
+"Tests" list of the re-vendoring commit on the same page): three input
+families, the worst of five seeds, token counts on both sides of each route
+edge, both rstd forms, and the FP32-eager criterion. A program fails that
+criterion when its worst dw error exceeds that of the FP32 eager computation
+on the same inputs (FP32 weight) or its median dw error exceeds the eager
+median (either weight dtype). The eager computation is torch in float32 on
+the GPU: dw = sum over t of dy * (x * rstd).
+
+Each case prints the worst error as a fraction of the budget.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import bwd_rmsnorm_fwd_02_amd as rn
+import oracle
+from tests import synth
+from tests.parity import DW_ATOL, DW_RTOL, oracle_rstd32
+from tests.test_parity_gpu import DEV, dev_bf16, dev_f32, dev_w
+
+pytestmark = pytest.mark.gpu
+
+SEEDS = range(5)
+
+# (T, H, w dtype): both sides of the small-T edge (64 | 65), of the
+# FP32 | FP64 partial switch (8192 | 8193), and mid-size rows of each width
+# class in the route table.
+EDGES = [
+    (64, 256, "f32"), (65, 256, "f32"),
+    (64, 4096, "bf16"), (65, 4096, "bf16"),
+    (8192, 1024, "f32"), (8193, 1024, "f32"),
+    (4097, 2048, "bf16"), (12000, 5120, "f32"),
+    (20000, 256, "bf16"),
+]
+
+
+def _errors(dw, dw64):
+    return np.abs(np.asarray(dw, np.float64) - dw64)
+
+
+@pytest.mark.parametrize("family", list(synth.FAMILIES))
+@pytest.mark.parametrize("T,H,wdt", EDGES)
+def test_dw_accuracy_sweep(family, T, H, wdt):
+    worst = {True: 0.0, False: 0.0}
+    worst_eager = 0.0
+    ours_med, eager_med = [], []
+    ours_max, eager_max = [], []
+    for seed in SEEDS:
+        wl = synth.make(T=T, H=H, w_dtype=wdt, seed=1000 * seed + T + H, **synth.FAMILIES[family])
+        r64, r32 = oracle_rstd32(wl.x, wl.w.f64, wl.eps)
+        _, _, dw64 = oracle.bwd(wl.dy, wl.x, r32.astype(np.float64), wl.w.f64, want_dx=False)
+        _, _, dw64_i = oracle.bwd(wl.dy, wl.x, r64, wl.w.f64, want_dx=False)
+        tol = DW_ATOL + DW_RTOL * np.abs(dw64)
+        tol_i = DW_ATOL + DW_RTOL * np.abs(dw64_i)
+        x, dy, w, rs = dev_bf16(wl.x), dev_bf16(wl.dy), dev_w(wl.w), dev_f32(r32)
+        for det in (True, False):
+            _, dw = rn.rmsnorm_bwd(dy, x, rs, w, deterministic=det)
+            torch.cuda.synchronize()
+            dwn = dw.cpu().numpy()
+            e = _errors(dwn, dw64)
+            worst[det] = max(worst[det], float(np.max(e / tol)), float(np.max(_errors(dwn, dw64_i) / tol_i)))
+            if det:
+                ours_med.append(float(np.median(e)))
+                ours_max.append(float(np.max(e)))
+        eager = (dy.float() * (x.float() * rs[:, None])).sum(0)
+        torch.cuda.synchronize()
+        ee = _errors(eager.cpu().numpy(), dw64)
+        eager_med.append(float(np.median(ee)))
+        eager_max.append(float(np.max(ee)))
+        worst_eager = max(worst_eager, float(np.max(ee / tol)))
+    print(f"family={family} T={T} H={H} w={wdt}: worst dw err/budget det {worst[True]:.2e} "
+          f"non-det {worst[False]:.2e}; FP32 eager {worst_eager:.2e}", flush=True)
+    assert worst[True] <= 1.0 and worst[False] <= 1.0
+    if wdt == "f32":
+        assert max(ours_max) <= max(eager_max), "worst dw error above the FP32 eager reference's"
+    assert np.median(ours_med) <= np.median(eager_med), "median dw error above the FP32 eager median"
