@@ -9,20 +9,34 @@ synthetic tensors already resident in HBM. Consecutive steps rotate over
 enough buffer sets (>= 1 GiB in the cycle) that no step finds its tensors in
 the 256 MB Infinity Cache, so the figure is an HBM figure.
 
+--op picks what a step is (the pages time fwd, bwd and "2xfwd+bwd", the
+checkpointed step: forward, forward recompute, backward):
+  fwd+bwd (default)    forward, backward
+  fwd | bwd            one of them (the backward reads the rstd and h that
+                       a forward left in the same buffer set beforehand)
+  2xfwd+bwd            forward, forward again (recompute), backward
+  fwd+bwd_recompute    forward, then the backward that recomputes rstd from
+                       x itself (plain forms): the checkpointed step with the
+                       recompute forward folded into the backward
+
 Timing:
 * value: K steps captured in one HIP graph (the pages time graph replays),
-  replayed once between two synchronisations; GB/s of algorithmic bytes.
+  replayed --replays times, each between two synchronisations; the median
+  replay gives ms_per_step; GB/s of algorithmic bytes.
 * roofline: the same K steps launched eagerly with the library's per-kernel
   HIP-event timers on the launch stream; the dominant kernel is the
-  backward row kernel; achieved = its algorithmic bytes per launch / its
-  mean event-timed duration; peak = 8 TB/s.
-* cpu_baseline: the FP64 oracle, single-threaded, on the same workload.
+  backward row kernel (the forward for --op fwd); achieved = its
+  algorithmic bytes per launch / its mean event-timed duration; peak 8 TB/s.
+* cpu_baseline: the FP64 oracle on the same work, called on row slices from
+  a pool of host threads (the oracle's C code runs without the interpreter
+  lock), and single-threaded beside it.
 
 Prints one JSON line.
 """
 from __future__ import annotations
 
 import argparse
+import concurrent.futures as cf
 import ctypes
 import json
 import math
@@ -37,6 +51,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBPS = 8000.0
 METRIC = "RMSNorm fwd+bwd effective HBM GB/s and % of 8 TB/s peak, per (T,H)"
 DEFAULT_CONFIG = "c2_T4096_H4096_bf16w"
+OPS = ("fwd+bwd", "fwd", "bwd", "2xfwd+bwd", "fwd+bwd_recompute")
 
 
 def algorithmic_bytes(rows: int, H: int, sw: int, residual: bool, with_dres: bool):
@@ -54,8 +69,13 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=400)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", default=DEFAULT_CONFIG)
+    ap.add_argument("--op", choices=OPS, default="fwd+bwd")
+    ap.add_argument("--replays", type=int, default=5)
     ap.add_argument("--seed", type=int, default=0)
-    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="seconds of oracle work for each of the two CPU runs")
+    ap.add_argument("--cpu-threads", type=int, default=0,
+                    help="host threads for the oracle run (0: min(16, CPUs))")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES bytes 10 times (the reference "
@@ -96,7 +116,17 @@ def main() -> int:
     sw = 2 if wl.w.dtype == "bf16" else 4
     wdt = _lib.RMSN_BF16 if wl.w.dtype == "bf16" else _lib.RMSN_F32
     fwd_b, bwd_row_b, bwd_b = algorithmic_bytes(rows, H, sw, residual, with_dres)
-    step_bytes = fwd_b + bwd_b
+    op = args.op
+    rc = op == "fwd+bwd_recompute"
+    if rc and residual:
+        print("--op fwd+bwd_recompute covers the plain and per-head forms only", file=sys.stderr)
+        return 2
+    if rc:  # the recompute backward reads no rstd
+        bwd_row_b -= 4 * rows
+        bwd_b -= 4 * rows
+    n_fwd = {"fwd+bwd": 1, "fwd": 1, "bwd": 0, "2xfwd+bwd": 2, "fwd+bwd_recompute": 1}[op]
+    has_bwd = op != "fwd"
+    step_bytes = n_fwd * fwd_b + (bwd_b if has_bwd else 0)
 
     def d16(bits):
         return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
@@ -140,37 +170,57 @@ def main() -> int:
         xv = _lib.View(T, heads, H, heads * H, H)
     cv = _lib.View(T, heads, H, heads * H, H)
 
-    def step(s, det: int, stream):
-        wsp, ws_bytes = ws_arg[det]
+    dxv = xv if wl.xbuf is not None else cv
+
+    def fwd(s, stream):
         if residual:
             _lib.check(lib.rmsnorm_residual_fwd(P(s["x"].data_ptr()), P(s["r"].data_ptr()),
                                                 P(w.data_ptr()), wdt, ctypes.c_float(wl.eps),
                                                 P(s["h"].data_ptr()), P(s["y"].data_ptr()),
                                                 P(s["rstd"].data_ptr()), rows, H, stream))
+        else:
+            _lib.check(lib.rmsnorm_fwd_strided(P(s["x"].data_ptr()), xv, P(w.data_ptr()), wdt,
+                                               ctypes.c_float(wl.eps), P(s["y"].data_ptr()), cv,
+                                               P(s["rstd"].data_ptr()), stream))
+
+    def bwd(s, det: int, stream):
+        wsp, ws_bytes = ws_arg[det]
+        if residual:
             _lib.check(lib.rmsnorm_residual_bwd(P(s["dy"].data_ptr()), P(s["h"].data_ptr()),
                                                 P(s["dres"].data_ptr()) if with_dres else None,
                                                 P(s["rstd"].data_ptr()), P(w.data_ptr()), wdt, det,
                                                 P(s["dx"].data_ptr()), P(s["dw"].data_ptr()), rows, H,
                                                 wsp, ws_bytes, stream))
+        elif rc:
+            _lib.check(lib.rmsnorm_bwd_recompute(P(s["dy"].data_ptr()), cv, P(s["x"].data_ptr()), xv,
+                                                 P(w.data_ptr()), wdt, ctypes.c_float(wl.eps), det,
+                                                 P(s["dx"].data_ptr()), dxv, P(s["dw"].data_ptr()),
+                                                 wsp, ws_bytes, stream))
         else:
-            _lib.check(lib.rmsnorm_fwd_strided(P(s["x"].data_ptr()), xv, P(w.data_ptr()), wdt,
-                                               ctypes.c_float(wl.eps), P(s["y"].data_ptr()), cv,
-                                               P(s["rstd"].data_ptr()), stream))
             _lib.check(lib.rmsnorm_bwd_strided(P(s["dy"].data_ptr()), cv, P(s["x"].data_ptr()), xv,
                                                P(s["rstd"].data_ptr()), P(w.data_ptr()), wdt, det,
-                                               P(s["dx"].data_ptr()), xv if wl.xbuf is not None else cv,
-                                               P(s["dw"].data_ptr()), wsp, ws_bytes, stream))
+                                               P(s["dx"].data_ptr()), dxv, P(s["dw"].data_ptr()),
+                                               wsp, ws_bytes, stream))
+
+    def step(s, det: int, stream):
+        for _ in range(n_fwd):
+            fwd(s, stream)
+        if has_bwd:
+            bwd(s, det, stream)
 
     K, W = args.steps, args.warmup
     cur = torch.cuda.current_stream(dev)
     sp = P(cur.cuda_stream)
 
-    # eager warm-up, then a reference result for set 0
+    # every set gets a forward's rstd (and h) first, so a backward-only step
+    # has its inputs; then the eager warm-up and a reference result for set 0
+    for s in sets:
+        fwd(s, sp)
     for i in range(W):
         step(sets[i % n_sets], 1, sp)
     torch.cuda.synchronize()
-    ref_dx = sets[0]["dx"].clone()
-    ref_dw = sets[0]["dw"].clone()
+    out_keys = (["y"] if n_fwd else []) + (["dx", "dw"] if has_bwd else [])
+    ref = {k: sets[0][k].clone() for k in out_keys}
 
     def capture(det: int):
         g = torch.cuda.CUDAGraph()
@@ -184,31 +234,49 @@ def main() -> int:
         torch.cuda.synchronize()
         return g
 
-    def timed_replay(g):
+    def same_bits(a, b):
+        return torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a.view(torch.int32),
+                           b.view(torch.int16) if b.dtype == torch.bfloat16 else b.view(torch.int32))
+
+    def timed_replays(g, check: bool):
+        """Median wall and GPU ms of --replays replays; every replay of the
+        deterministic graph must reproduce the eager result bit for bit."""
         g.replay()  # warm
         torch.cuda.synchronize()
-        sets[0]["dx"].zero_()
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        e0.record()
-        g.replay()
-        e1.record()
-        torch.cuda.synchronize()
-        t1 = time.perf_counter()
-        return (t1 - t0) * 1e3, e0.elapsed_time(e1)
+        walls, gpus = [], []
+        for _ in range(max(1, args.replays)):
+            for k in out_keys:
+                sets[0][k].zero_()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            e0.record()
+            g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            walls.append((time.perf_counter() - t0) * 1e3)
+            gpus.append(e0.elapsed_time(e1))
+            if check:
+                for k in out_keys:
+                    assert same_bits(sets[0][k], ref[k]), f"graph {k} != eager"
+        walls.sort()
+        gpus.sort()
+        return walls, gpus
 
     g_det = capture(1)
-    wall_ms, gpu_ms = timed_replay(g_det)
-    # every replay must reproduce the eager deterministic result
-    assert torch.equal(sets[0]["dx"].view(torch.int16), ref_dx.view(torch.int16)), "graph dx != eager"
-    assert torch.equal(sets[0]["dw"].view(torch.int32), ref_dw.view(torch.int32)), "graph dw != eager"
+    walls, gpus = timed_replays(g_det, check=True)
     del g_det
-    g_nd = capture(0)
-    wall_nd_ms, gpu_nd_ms = timed_replay(g_nd)
-    del g_nd
+    walls_nd = None
+    if has_bwd:
+        g_nd = capture(0)
+        walls_nd, _ = timed_replays(g_nd, check=False)
+        del g_nd
 
+    def median(v):
+        n = len(v)
+        return v[n // 2] if n % 2 else 0.5 * (v[n // 2 - 1] + v[n // 2])
+
+    wall_ms, gpu_ms = median(walls), median(gpus)
     ms_per_step = wall_ms / K
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
 
@@ -236,7 +304,9 @@ def main() -> int:
     bwd_row_us = avg_us(_lib.RMSN_TIMER_BWD_ROW)
     reduce_us = avg_us(_lib.RMSN_TIMER_DW_REDUCE)
     small_us = avg_us(_lib.RMSN_TIMER_BWD_SMALL)
-    if bwd_row_us is not None:
+    if not has_bwd:
+        dom_name, dom_us, dom_bytes = "fwd", fwd_us, fwd_b
+    elif bwd_row_us is not None:
         dom_name, dom_us, dom_bytes = "bwd_row", bwd_row_us, bwd_row_b
     else:
         dom_name, dom_us, dom_bytes = "bwd_small", small_us, bwd_b
@@ -244,7 +314,7 @@ def main() -> int:
 
     traffic = None
     tr_path = os.path.join(ROOT, "profiles", f"traffic_{args.config}.json")
-    if os.path.exists(tr_path):
+    if os.path.exists(tr_path) and op == "fwd+bwd":
         from bwd_rmsnorm_fwd_02_amd import build as _b
         rec = json.load(open(tr_path))
         if rec.get("source_hash") == _b.source_hash() and dom_name in rec.get("kernels", {}):
@@ -257,18 +327,37 @@ def main() -> int:
     cpu = None
     if not args.no_cpu_baseline:
         import oracle
-        t_start = time.perf_counter()
-        reps = 0
-        # the whole workload: forward, then backward at the oracle's rstd
+        # the same work as one step: the forward (n_fwd times; the recompute
+        # backward is the forward's statistics plus the backward), then the
+        # backward at the oracle's rstd
         xo = wl.x if not residual else oracle.residual_add(wl.x, wl.r)
-        while True:
-            r64, y64 = oracle.fwd(xo, wl.w.f64, wl.eps)
-            oracle.bwd(wl.dy, xo, r64, wl.w.f64)
-            reps += 1
-            el = time.perf_counter() - t_start
-            if el >= args.cpu_seconds:
-                break
-        cpu_gbps = step_bytes * reps / el / 1e9
+        w64 = wl.w.f64
+        r_all, _ = oracle.fwd(xo, w64, wl.eps, want_y=False)
+
+        def oracle_rows(lo, hi):
+            r64 = r_all[lo:hi]
+            for _ in range(n_fwd):
+                r64, _ = oracle.fwd(xo[lo:hi], w64, wl.eps)
+            if rc:
+                r64, _ = oracle.fwd(xo[lo:hi], w64, wl.eps, want_y=False)
+            if has_bwd:
+                oracle.bwd(wl.dy[lo:hi], xo[lo:hi], r64, w64)
+
+        def run(threads):
+            bounds = [(rows * i // threads, rows * (i + 1) // threads) for i in range(threads)]
+            reps = 0
+            t_start = time.perf_counter()
+            with cf.ThreadPoolExecutor(max_workers=threads) as ex:
+                while True:
+                    list(ex.map(lambda b: oracle_rows(*b), bounds))
+                    reps += 1
+                    el = time.perf_counter() - t_start
+                    if el >= args.cpu_seconds:
+                        return reps, el
+
+        threads = args.cpu_threads or min(16, os.cpu_count() or 1)
+        reps_n, el_n = run(threads)
+        reps_1, el_1 = run(1)
         model = ""
         try:
             for line in open("/proc/cpuinfo"):
@@ -277,12 +366,16 @@ def main() -> int:
                     break
         except OSError:
             pass
-        cpu = {"value": round(cpu_gbps, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-               "sample": f"the full {args.config} workload (fwd + bwd, FP64), {reps} repetition(s) "
-                         f"in {el:.1f} s on one thread of {model or platform.processor()}"}
+        cpu = {"value": round(step_bytes * reps_n / el_n / 1e9, 4), "unit": "GB/s", "cores": threads,
+               "kind": "oracle",
+               "sample": f"the full {args.config} workload ({op}, FP64 oracle), {reps_n} repetition(s) "
+                         f"in {el_n:.1f} s, rows split over {threads} host threads of "
+                         f"{model or platform.processor()}",
+               "single_thread": {"value": round(step_bytes * reps_1 / el_1 / 1e9, 4), "cores": 1,
+                                 "sample": f"{reps_1} repetition(s) in {el_1:.1f} s"}}
 
     out = {
-        "metric": METRIC,
+        "metric": METRIC if op == "fwd+bwd" else f"RMSNorm {op} effective HBM GB/s, per (T,H)",
         "value": round(value, 2),
         "unit": "GB/s",
         "n_gpus": 1,
@@ -294,15 +387,18 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": args.config, "T": T, "heads": heads, "H": H,
+        "config": {"workload": args.config, "op": op, "T": T, "heads": heads, "H": H,
                    "w_dtype": wl.w.dtype, "residual": residual, "deterministic": True,
                    "global_batch": rows, "seq_len": T, "parallelism": "none (1 GPU)",
                    "buffer_sets": n_sets},
+        "replay_ms_per_step": {"median": round(ms_per_step, 5), "min": round(walls[0] / K, 5),
+                               "max": round(walls[-1] / K, 5), "replays": len(walls)},
         "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBPS, 2),
         "fwd_GBps": round(fwd_gbps, 1) if fwd_gbps else None,
         "bwd_GBps": round(bwd_gbps, 1) if bwd_gbps else None,
-        "nondeterministic": {"ms_per_step": round(wall_nd_ms / K, 5),
-                             "value": round(step_bytes / (wall_nd_ms / K * 1e-3) / 1e9, 2)},
+        "nondeterministic": ({"ms_per_step": round(median(walls_nd) / K, 5),
+                              "value": round(step_bytes / (median(walls_nd) / K * 1e-3) / 1e9, 2)}
+                             if walls_nd else None),
         "kernel_us": {"fwd": fwd_us, "bwd_row": bwd_row_us, "dw_reduce": reduce_us,
                       "bwd_small": small_us},
         "graph_gpu_ms": round(gpu_ms, 4),

@@ -186,6 +186,29 @@ def rmsnorm_bwd_strided(dy: torch.Tensor, x: torch.Tensor, rstd: torch.Tensor, w
     return dx, dw
 
 
+def rmsnorm_bwd_recompute(dy: torch.Tensor, x: torch.Tensor, w: torch.Tensor, eps: float = 1e-6,
+                          deterministic: bool = True, dx: Optional[torch.Tensor] = None,
+                          dw: Optional[torch.Tensor] = None,
+                          workspace: Optional[torch.Tensor] = None):
+    """Backward without the forward's rstd (recomputed from x in the kernel),
+    over [T, H] or [T, heads, H] views; dw sums over T and heads."""
+    _need_bf16("dy", dy)
+    _need_bf16("x", x)
+    xv = _view(x)
+    rows = xv.T * xv.heads
+    if dx is None:
+        dx = torch.empty(x.shape, dtype=torch.bfloat16, device=x.device)
+    dw = torch.empty(xv.H, dtype=torch.float32, device=x.device) if dw is None else dw
+    need = rmsnorm_bwd_workspace_bytes(rows, xv.H, w.dtype, deterministic)
+    ws = workspace if workspace is not None else _workspace(x.device, need)
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _lib.check(_lib.load().rmsnorm_bwd_recompute(_ptr(dy), _view(dy), _ptr(x), xv, _ptr(w),
+                                                 _wdtype(w), float(eps), int(bool(deterministic)),
+                                                 _ptr(dx), _view(dx), _ptr(dw), _ptr(ws), nbytes,
+                                                 _stream(x.device)))
+    return dx, dw
+
+
 def rmsnorm_residual_bwd(dy: torch.Tensor, h: torch.Tensor, rstd: torch.Tensor, w: torch.Tensor,
                          dres: Optional[torch.Tensor] = None, deterministic: bool = True,
                          dh: Optional[torch.Tensor] = None, dw: Optional[torch.Tensor] = None,
@@ -213,12 +236,15 @@ def rmsnorm_status_string(status: int) -> str:
 
 
 def rmsnorm_route_query(op: str, rows: int, H: int, w_dtype: torch.dtype = torch.bfloat16,
-                        deterministic: bool = True, residual: bool = False) -> dict:
-    """Route-table entry for op 'fwd' or 'bwd' (host only, no GPU needed)."""
+                        deterministic: bool = True, residual: bool = False,
+                        recompute: bool = False) -> dict:
+    """Route-table entry for op 'fwd' or 'bwd' (host only, no GPU needed);
+    the backward form is plain, residual or recompute."""
     info = _lib.RouteInfo()
     wd = _lib.RMSN_BF16 if w_dtype == torch.bfloat16 else _lib.RMSN_F32
+    form = 2 if recompute else (1 if residual else 0)
     _lib.check(_lib.load().rmsnorm_route_query(0 if op == "fwd" else 1, rows, H, wd,
-                                               int(bool(deterministic)), int(bool(residual)),
+                                               int(bool(deterministic)), form,
                                                ctypes.byref(info)))
     return info.as_dict()
 

@@ -37,7 +37,8 @@ STATUS = {
 EXPORTS = [
     "rmsnorm_fwd", "rmsnorm_fwd_strided", "rmsnorm_residual_fwd",
     "rmsnorm_bwd_workspace_bytes", "rmsnorm_workspace_init", "rmsnorm_bwd",
-    "rmsnorm_bwd_strided", "rmsnorm_residual_bwd", "rmsnorm_status_string",
+    "rmsnorm_bwd_strided", "rmsnorm_bwd_recompute", "rmsnorm_residual_bwd",
+    "rmsnorm_status_string",
     "rmsnorm_route_query", "rmsnorm_route_override", "rmsnorm_timing_enable",
     "rmsnorm_timing_read",
 ]
@@ -95,6 +96,7 @@ def load() -> ctypes.CDLL:
         "rmsnorm_workspace_init": [p, sz, p],
         "rmsnorm_bwd": [p, p, p, p, i32, i32, p, p, i64, i64, p, sz, p],
         "rmsnorm_bwd_strided": [p, View, p, View, p, p, i32, i32, p, View, p, p, sz, p],
+        "rmsnorm_bwd_recompute": [p, View, p, View, p, i32, f32, i32, p, View, p, p, sz, p],
         "rmsnorm_residual_bwd": [p, p, p, p, p, i32, i32, p, p, i64, i64, p, sz, p],
         "rmsnorm_status_string": [i32],
         "rmsnorm_route_query": [i32, i64, i64, i32, i32, i32, ctypes.POINTER(RouteInfo)],

@@ -180,7 +180,7 @@ int fwd_impl(const void* x, const rmsn_view_t& xv, const void* r, const rmsn_vie
     }
 
     Route rt;
-    if ((st = route(0, rows, xv.H, wdt, 1, residual, &rt)) != RMSN_OK) return st;
+    if ((st = route(0, rows, xv.H, wdt, 1, kFormPlain, &rt)) != RMSN_OK) return st;
     FwdParams p;
     memset(&p, 0, sizeof p);
     p.x = static_cast<const uint16_t*>(x);
@@ -213,9 +213,12 @@ int fwd_impl(const void* x, const rmsn_view_t& xv, const void* r, const rmsn_vie
 int bwd_impl(const void* dy, const rmsn_view_t& dyv, const void* x, const rmsn_view_t& xv,
              const void* dres, const rmsn_view_t* resv, const float* rstd, const void* w,
              rmsn_dtype_t wdt, int det, void* dx, const rmsn_view_t& dxv, float* dw,
-             void* ws, size_t ws_bytes, bool residual, hipStream_t s) {
+             void* ws, size_t ws_bytes, int form, float eps, hipStream_t s) {
+    const bool residual = form == kFormResidual;
+    const bool rc = form == kFormRecompute;  // rstd recomputed from x, none passed
     int st;
     if ((st = check_dtype(wdt)) != RMSN_OK) return st;
+    if (rc && (st = check_eps(eps)) != RMSN_OK) return st;
     if ((st = check_shape(xv)) != RMSN_OK) return st;
     if ((st = check_shape(dyv)) != RMSN_OK) return st;
     if ((st = check_shape(dxv)) != RMSN_OK) return st;
@@ -232,9 +235,9 @@ int bwd_impl(const void* dy, const rmsn_view_t& dyv, const void* x, const rmsn_v
         timer_end(RMSN_TIMER_INIT, s);
         return st;
     }
-    if (!x || !dy || !rstd || !w || !dx) return RMSN_ERR_NULL;
+    if (!x || !dy || (!rc && !rstd) || !w || !dx) return RMSN_ERR_NULL;
     if (residual && resv && !dres) return RMSN_ERR_NULL;
-    if (!aligned(w, 16) || !aligned(rstd, 4)) return RMSN_ERR_ALIGN;
+    if (!aligned(w, 16) || (!rc && !aligned(rstd, 4))) return RMSN_ERR_ALIGN;
     int64_t ex, edy, edx, eres = 0;
     if ((st = check_layout(x, xv, &ex)) != RMSN_OK) return st;
     if ((st = check_layout(dy, dyv, &edy)) != RMSN_OK) return st;
@@ -243,7 +246,8 @@ int bwd_impl(const void* dy, const rmsn_view_t& dyv, const void* x, const rmsn_v
     if (!rows_disjoint(dxv)) return RMSN_ERR_ALIAS;
 
     const Span sx = span_of(x, ex, 2), sdy = span_of(dy, edy, 2), sdx = span_of(dx, edx, 2);
-    const Span sw = span_of(w, H, wsize(wdt)), srs = span_of(rstd, rows, 4);
+    const Span sw = span_of(w, H, wsize(wdt));
+    const Span srs = rc ? Span{0, 0} : span_of(rstd, rows, 4);
     const Span sdw = span_of(dw, H, 4);
     const Span sres = dres ? span_of(dres, eres, 2) : Span{0, 0};
     if (overlap(sdx, sx) || overlap(sdx, sdy) || overlap(sdx, sw) || overlap(sdx, srs) ||
@@ -253,7 +257,7 @@ int bwd_impl(const void* dy, const rmsn_view_t& dyv, const void* x, const rmsn_v
         return RMSN_ERR_ALIAS;
 
     Route rt;
-    if ((st = route(1, rows, H, wdt, det, residual, &rt)) != RMSN_OK) return st;
+    if ((st = route(1, rows, H, wdt, det, form, &rt)) != RMSN_OK) return st;
     if (rt.workspace > 0) {
         if (!ws || !aligned(ws, 256) || ws_bytes < rt.workspace) return RMSN_ERR_WORKSPACE;
         const Span sws = span_of(ws, (int64_t)rt.workspace, 1);
@@ -281,6 +285,7 @@ int bwd_impl(const void* dy, const rmsn_view_t& dyv, const void* x, const rmsn_v
     p.nvec = (int32_t)(H / kVec);
     p.tpr = rt.r.lanes_per_row;
     p.rpb = rt.r.rows_per_block;
+    p.eps = eps;
 
     if (rt.r.kind == RMSN_KIND_BWD_COLTASK) {
         p.ncol_blocks = (int32_t)rt.r.reduce_grid;
@@ -293,7 +298,7 @@ int bwd_impl(const void* dy, const rmsn_view_t& dyv, const void* x, const rmsn_v
     if (rt.r.kind == RMSN_KIND_BWD_ROW_DET) {
         p.partial = ws;
         timer_begin(RMSN_TIMER_BWD_ROW, s);
-        st = launch_bwd_row(p, rt, wdt, residual, s);
+        st = launch_bwd_row(p, rt, wdt, form, s);
         timer_end(RMSN_TIMER_BWD_ROW, s);
         if (st != RMSN_OK) return st;
         timer_begin(RMSN_TIMER_DW_REDUCE, s);
@@ -310,7 +315,7 @@ int bwd_impl(const void* dy, const rmsn_view_t& dyv, const void* x, const rmsn_v
     timer_end(RMSN_TIMER_INIT, s);
     if (st != RMSN_OK) return st;
     timer_begin(RMSN_TIMER_BWD_ROW, s);
-    st = launch_bwd_row(p, rt, wdt, residual, s);
+    st = launch_bwd_row(p, rt, wdt, form, s);
     timer_end(RMSN_TIMER_BWD_ROW, s);
     return st;
 }
@@ -342,12 +347,14 @@ int rmsnorm_residual_fwd(const void* x, const void* r, const void* w, rmsn_dtype
 
 size_t rmsnorm_bwd_workspace_bytes(int64_t rows, int64_t H, rmsn_dtype_t w_dtype,
                                    int deterministic) {
-    Route rt;
-    if (route(1, rows, H, w_dtype, deterministic, 0, &rt) != RMSN_OK) return 0;
-    Route rr;
-    if (route(1, rows, H, w_dtype, deterministic, 1, &rr) == RMSN_OK && rr.workspace > rt.workspace)
-        return rr.workspace;
-    return rt.workspace;
+    // the largest need over the three backward forms
+    size_t need = 0;
+    for (int form : {kFormPlain, kFormResidual, kFormRecompute}) {
+        Route rt;
+        if (route(1, rows, H, w_dtype, deterministic, form, &rt) == RMSN_OK && rt.workspace > need)
+            need = rt.workspace;
+    }
+    return need;
 }
 
 int rmsnorm_workspace_init(void* workspace, size_t workspace_bytes, hipStream_t stream) {
@@ -364,7 +371,7 @@ int rmsnorm_bwd(const void* dy, const void* x, const float* rstd, const void* w,
                 int64_t H, void* workspace, size_t workspace_bytes, hipStream_t stream) {
     const rmsn_view_t v = contiguous(T, H);
     return bwd_impl(dy, v, x, v, nullptr, nullptr, rstd, w, w_dtype, deterministic, dx, v, dw,
-                    workspace, workspace_bytes, false, stream);
+                    workspace, workspace_bytes, kFormPlain, 0.f, stream);
 }
 
 int rmsnorm_bwd_strided(const void* dy, rmsn_view_t dyv, const void* x, rmsn_view_t xv,
@@ -372,7 +379,15 @@ int rmsnorm_bwd_strided(const void* dy, rmsn_view_t dyv, const void* x, rmsn_vie
                         void* dx, rmsn_view_t dxv, float* dw, void* workspace,
                         size_t workspace_bytes, hipStream_t stream) {
     return bwd_impl(dy, dyv, x, xv, nullptr, nullptr, rstd, w, w_dtype, deterministic, dx, dxv, dw,
-                    workspace, workspace_bytes, false, stream);
+                    workspace, workspace_bytes, kFormPlain, 0.f, stream);
+}
+
+int rmsnorm_bwd_recompute(const void* dy, rmsn_view_t dyv, const void* x, rmsn_view_t xv,
+                          const void* w, rmsn_dtype_t w_dtype, float eps, int deterministic,
+                          void* dx, rmsn_view_t dxv, float* dw, void* workspace,
+                          size_t workspace_bytes, hipStream_t stream) {
+    return bwd_impl(dy, dyv, x, xv, nullptr, nullptr, nullptr, w, w_dtype, deterministic, dx, dxv,
+                    dw, workspace, workspace_bytes, kFormRecompute, eps, stream);
 }
 
 int rmsnorm_residual_bwd(const void* dy, const void* h, const void* dres, const float* rstd,
@@ -381,7 +396,7 @@ int rmsnorm_residual_bwd(const void* dy, const void* h, const void* dres, const 
                          hipStream_t stream) {
     const rmsn_view_t v = contiguous(T, H);
     return bwd_impl(dy, v, h, v, dres, dres ? &v : nullptr, rstd, w, w_dtype, deterministic, dh, v,
-                    dw, workspace, workspace_bytes, true, stream);
+                    dw, workspace, workspace_bytes, kFormResidual, 0.f, stream);
 }
 
 const char* rmsnorm_status_string(int status) {
@@ -409,10 +424,10 @@ const char* rmsnorm_status_string(int status) {
 }
 
 int rmsnorm_route_query(int op, int64_t rows, int64_t H, rmsn_dtype_t w_dtype, int deterministic,
-                        int residual, rmsn_route_t* out) {
+                        int form, rmsn_route_t* out) {
     if (!out) return RMSN_ERR_NULL;
     Route rt;
-    const int st = route(op, rows, H, w_dtype, deterministic, residual, &rt);
+    const int st = route(op, rows, H, w_dtype, deterministic, op == 0 ? kFormPlain : form, &rt);
     *out = rt.r;
     return st;
 }

@@ -3,8 +3,8 @@
 
 namespace rmsn {
 
-int launch_bwd_row_bf16w(const BwdParams& p, const Route& rt, bool residual, hipStream_t s) {
-    return launch_bwd_row_wt<uint16_t>(p, rt, residual, s);
+int launch_bwd_row_bf16w(const BwdParams& p, const Route& rt, int form, hipStream_t s) {
+    return launch_bwd_row_wt<uint16_t>(p, rt, form, s);
 }
 
 int launch_bwd_small_bf16w(const BwdParams& p, const Route& rt, bool residual, hipStream_t s) {

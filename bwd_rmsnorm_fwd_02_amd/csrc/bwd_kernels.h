@@ -28,6 +28,13 @@
 //   counter) converts it to FP32 dw.
 // * small T: one launch of k_bwd_small — column tasks sum whole columns over
 //   every row in a fixed row order while row tasks produce dx.
+//
+// Recompute form (RC): the row kernel takes no rstd input and forms each
+// row's rstd from the x row it already holds, with the forward's arithmetic
+// (FP32 sums of squares per 16-byte vector, added in FP64, one rounding of
+// 1/sqrt(mean + eps) to FP32). For activation recompute, where a training
+// step runs the forward, the forward again, then the backward (the pages'
+// "2xfwd+bwd"), this serves callers that kept x but not rstd.
 #pragma once
 
 #include "rmsn_device.h"
@@ -51,7 +58,7 @@ struct BwdTile {
 // around memory operations (branches there make the compiler's wait counting
 // fall back to waiting for everything). Without a residual gradient the dres
 // slot reloads dy, which stays unused.
-template <int NV, int U, bool RES>
+template <int NV, int U, bool RES, bool RC = false>
 __device__ __forceinline__ void bwd_load(const BwdParams& p, int64_t r0, int64_t rend, int slot,
                                          int lr, BwdTile<NV, U, RES>& t) {
 #pragma unroll
@@ -79,11 +86,11 @@ __device__ __forceinline__ void bwd_load(const BwdParams& p, int64_t r0, int64_t
             t.dy[k][v] = ld16(p.dy + ody + c);
             if constexpr (RES) t.dres[k][v] = ld16(rsrc + ores + c);
         }
-        t.rs[k] = p.rstd[r];
+        if constexpr (!RC) t.rs[k] = p.rstd[r];
     }
 }
 
-template <int NV, int U, bool RES>
+template <int NV, int U, bool RES, bool RC = false>
 __device__ __forceinline__ void bwd_ready(const BwdTile<NV, U, RES>& t) {
 #pragma unroll
     for (int k = 0; k < U; ++k) {
@@ -93,52 +100,77 @@ __device__ __forceinline__ void bwd_ready(const BwdTile<NV, U, RES>& t) {
             use_now(t.dy[k][v]);
             if constexpr (RES) use_now(t.dres[k][v]);
         }
-        use_now(t.rs[k]);
+        if constexpr (!RC) use_now(t.rs[k]);
     }
 }
 
-// Row-group sums of U per-lane FP32 values. WIDE rows span several waves
-// and exchange wave sums through LDS, double-buffered by `buf` so that one
-// LDS-only barrier per iteration suffices. The order of every sum is fixed.
-template <int U, bool WIDE>
-__device__ __forceinline__ void row_sums(float (&v)[U], const BwdParams& p, int slot, int lr,
-                                         float* red, int& buf) {
+// Row-group sums of U per-lane FP32 values (the dot products) and, in the
+// recompute form, U FP64 values (the sums of squares). WIDE rows span
+// several waves and exchange wave sums through LDS (FP32 area `red`, FP64
+// area `redd`), double-buffered by `buf` so that one LDS-only barrier per
+// iteration suffices. The order of every sum is fixed; the dot products are
+// summed the same way in every form, so dx does not depend on the form. The
+// sums of squares take the vector-ALU reduction (wave_sums): they are exact
+// in FP64 in any order, and it keeps their exchange short.
+template <int U, bool WIDE, bool RC>
+__device__ __forceinline__ void row_sums(float (&dot)[U], double (&ss)[U], const BwdParams& p,
+                                         int slot, int lr, float* red, double* redd, int& buf) {
     if constexpr (WIDE) {
         const int wpr = p.tpr >> 6;
         const int wave = lr >> 6;
+        const int lane = lr & 63;
 #pragma unroll
         for (int k = 0; k < U; ++k) {
-            const float a = group_sum<64>(v[k]);
-            if ((lr & 63) == 0 && slot < p.rpb) red[((buf * p.rpb + slot) * U + k) * wpr + wave] = a;
+            const float a = group_sum<64>(dot[k]);
+            if (lane == 0 && slot < p.rpb) red[((buf * p.rpb + slot) * U + k) * wpr + wave] = a;
+        }
+        if constexpr (RC) {
+            // lane q < U holds the sum of squares of row wave_row<U>(q)
+            const double b = wave_sums<U>(ss, lane);
+            if (lane < U && slot < p.rpb)
+                redd[((buf * p.rpb + slot) * U + wave_row<U>(lane)) * wpr + wave] = b;
         }
         lds_barrier();
 #pragma unroll
         for (int k = 0; k < U; ++k) {
             float t = 0.f;
-            if (slot < p.rpb)
-                for (int i = 0; i < wpr; ++i) t += red[((buf * p.rpb + slot) * U + k) * wpr + i];
-            v[k] = t;
+            double q = 0.0;
+            if (slot < p.rpb) {
+                const int i0 = ((buf * p.rpb + slot) * U + k) * wpr;
+                for (int i = 0; i < wpr; ++i) {
+                    t += red[i0 + i];
+                    if constexpr (RC) q += redd[i0 + i];
+                }
+            }
+            dot[k] = t;
+            if constexpr (RC) ss[k] = q;
         }
         buf ^= 1;
     } else {
 #pragma unroll
-        for (int k = 0; k < U; ++k) v[k] = group_sum_rt(v[k], p.tpr);
+        for (int k = 0; k < U; ++k) {
+            dot[k] = group_sum_rt(dot[k], p.tpr);
+            if constexpr (RC) ss[k] = group_sum_rt(ss[k], p.tpr);
+        }
     }
 }
 
 // The backward of the rows held in a tile, up to the stores: dx (or dh)
 // packed into `out`, and, if ACC, dy*x*rstd added into acc for rows below
-// rend. No memory operation happens here except the LDS exchange.
-template <int NV, int U, bool RES, bool WIDE, bool ACC>
+// rend. No memory operation happens here except the LDS exchange of row
+// sums (`red` FP32, `redd` FP64 for the recompute form's sums of squares).
+template <int NV, int U, bool RES, bool WIDE, bool ACC, bool RC = false>
 __device__ __forceinline__ void bwd_compute(const BwdParams& p, int64_t r0, int64_t rend,
                                             int slot, int lr, const float (&wv)[NV][8],
                                             const bool (&vok)[NV], const BwdTile<NV, U, RES>& t,
                                             double (&acc)[NV][8], uint4 (&out)[U][NV], float* red,
-                                            int& buf) {
+                                            double* redd, int& buf) {
     float dot[U];
+    double ss[U];
 #pragma unroll
     for (int k = 0; k < U; ++k) {
         dot[k] = 0.f;
+        ss[k] = 0.0;
 #pragma unroll
         for (int v = 0; v < NV; ++v) {
             float xf[8], dyf[8];
@@ -148,14 +180,29 @@ __device__ __forceinline__ void bwd_compute(const BwdParams& p, int64_t r0, int6
 #pragma unroll
             for (int e = 0; e < 8; ++e) s = __builtin_fmaf(dyf[e] * wv[v][e], xf[e], s);
             if (vok[v]) dot[k] += s;
+            if constexpr (RC) {
+                // the forward's per-vector sum of squares, added in FP64
+                float q = xf[0] * xf[0];
+#pragma unroll
+                for (int e = 1; e < 8; ++e) q = __builtin_fmaf(xf[e], xf[e], q);
+                if (vok[v]) ss[k] += (double)q;
+            }
         }
     }
-    row_sums<U, WIDE>(dot, p, slot, lr, red, buf);
+    row_sums<U, WIDE, RC>(dot, ss, p, slot, lr, red, redd, buf);
+    float rsc[U];
+    if constexpr (RC) {
+#pragma unroll
+        for (int k = 0; k < U; ++k)
+            rsc[k] = (float)(1.0 / __builtin_sqrt(ss[k] / (double)p.H + (double)p.eps));
+    }
 #pragma unroll
     for (int k = 0; k < U; ++k) {
         const int64_t r = r0 + slot + (int64_t)k * p.rpb;
         const bool live = (slot < p.rpb) && (r < rend);
-        const float rs = t.rs[k];
+        float rs;
+        if constexpr (RC) rs = rsc[k];
+        else rs = t.rs[k];
         // c = (1/H) sum_j g_j * xhat_j = rstd * sum_j g_j x_j / H
         const float c = (dot[k] * rs) / (float)p.H;
         const double rs64 = (double)rs;
@@ -226,16 +273,19 @@ __device__ __forceinline__ void load_weights(const BwdParams& p, int slot, int l
 // Large-T row kernel: dx for the block's rows plus the block's dw sums.
 // Each iteration a row group takes U rows; with U <= 2 the next iteration's
 // rows are loaded before the current ones are processed.
-template <int NV, int U, typename WT, bool RES, bool WIDE, int MODE>
+template <int NV, int U, typename WT, bool RES, bool WIDE, int MODE, bool RC = false>
 __global__ void __launch_bounds__(WIDE ? (NV * U >= 4 ? 512 : 1024) : 256) k_bwd_row(BwdParams p) {
     constexpr bool PF = U <= 2;
     extern __shared__ double lds_bwd[];
     const int tid = threadIdx.x;
     const int slot = tid / p.tpr;
     const int lr = tid - slot * p.tpr;
-    // LDS: [H] doubles for the slot combine, then the row-sum exchange area
+    // LDS: [H] doubles for the slot combine, then (recompute form) the FP64
+    // exchange area, then the FP32 row-sum exchange area
     double* comb = lds_bwd;
-    float* red = reinterpret_cast<float*>(lds_bwd + (p.rpb > 1 ? p.H : 0));
+    double* redd = lds_bwd + (p.rpb > 1 ? p.H : 0);
+    const int nexch = WIDE ? 2 * p.rpb * U * (p.tpr >> 6) : 0;
+    float* red = reinterpret_cast<float*>(redd + (RC ? nexch : 0));
 
     float wv[NV][8];
     bool vok[NV];
@@ -261,22 +311,23 @@ __global__ void __launch_bounds__(WIDE ? (NV * U >= 4 ? 512 : 1024) : 256) k_bwd
     if (r0 < rend) {
         BwdTile<NV, U, RES> cur;
         BwdTile<NV, PF ? U : 1, RES> nxt;
-        bwd_load<NV, U, RES>(p, r0, rend, slot, lr, cur);
-        bwd_ready<NV, U, RES>(cur);
+        bwd_load<NV, U, RES, RC>(p, r0, rend, slot, lr, cur);
+        bwd_ready<NV, U, RES, RC>(cur);
 #pragma unroll 1
         for (; r0 < rend; r0 += stride) {
-            if constexpr (PF) bwd_load<NV, U, RES>(p, r0 + stride, rend, slot, lr, nxt);
+            if constexpr (PF) bwd_load<NV, U, RES, RC>(p, r0 + stride, rend, slot, lr, nxt);
             uint4 out[U][NV];
-            bwd_compute<NV, U, RES, WIDE, true>(p, r0, rend, slot, lr, wv, vok, cur, acc, out, red, buf);
+            bwd_compute<NV, U, RES, WIDE, true, RC>(p, r0, rend, slot, lr, wv, vok, cur, acc, out, red,
+                                                    redd, buf);
             // The next tile must be complete before its registers take over;
             // the wait lands before this iteration's stores are issued.
             if constexpr (PF) {
-                bwd_ready<NV, U, RES>(nxt);
+                bwd_ready<NV, U, RES, RC>(nxt);
                 cur = nxt;
             }
             bwd_store<NV, U>(p, r0, rend, slot, lr, vok, out);
             if constexpr (!PF) {
-                if (r0 + stride < rend) bwd_load<NV, U, RES>(p, r0 + stride, rend, slot, lr, cur);
+                if (r0 + stride < rend) bwd_load<NV, U, RES, RC>(p, r0 + stride, rend, slot, lr, cur);
             }
         }
     }
@@ -405,60 +456,65 @@ __global__ void __launch_bounds__(256) k_bwd_small(BwdParams p) {
     uint4 out[1][NV];
     bwd_load<NV, 1, RES>(p, rb, p.rows, slot, lr, t);
     if (p.tpr > 64)
-        bwd_compute<NV, 1, RES, true, false>(p, rb, p.rows, slot, lr, wv, vok, t, acc, out, red, buf);
+        bwd_compute<NV, 1, RES, true, false>(p, rb, p.rows, slot, lr, wv, vok, t, acc, out, red,
+                                             nullptr, buf);
     else
-        bwd_compute<NV, 1, RES, false, false>(p, rb, p.rows, slot, lr, wv, vok, t, acc, out, red, buf);
+        bwd_compute<NV, 1, RES, false, false>(p, rb, p.rows, slot, lr, wv, vok, t, acc, out, red,
+                                              nullptr, buf);
     bwd_store<NV, 1>(p, rb, p.rows, slot, lr, vok, out);
 }
 
 // ----------------------------------------------------------------- launchers
 
-inline size_t bwd_row_lds_bytes(const rmsn_route_t& r, int H) {
+inline size_t bwd_row_lds_bytes(const rmsn_route_t& r, int H, bool rc) {
     size_t lds = r.rows_per_block > 1 ? sizeof(double) * (size_t)H : 0;
-    if (r.lanes_per_row > 64)
-        lds += sizeof(float) * 2 * (size_t)r.rows_per_block * r.unroll * (r.lanes_per_row / 64);
+    if (r.lanes_per_row > 64) {
+        const size_t n = 2 * (size_t)r.rows_per_block * r.unroll * (r.lanes_per_row / 64);
+        lds += sizeof(float) * n;
+        if (rc) lds += sizeof(double) * n;
+    }
     return lds;
 }
 
-template <int NV, int U, typename WT, bool RES, bool WIDE>
+template <int NV, int U, typename WT, bool RES, bool WIDE, bool RC>
 static int launch_row_mode(const BwdParams& p, const Route& rt, size_t lds, hipStream_t s) {
     dim3 grid((unsigned)rt.r.grid), block((unsigned)rt.r.block_threads);
     if (rt.r.kind == RMSN_KIND_BWD_ROW_ATOMIC) {
         if constexpr (NV == 1 && U <= 2)
-            launch_kernel((k_bwd_row<NV, U, WT, RES, WIDE, kModeAtomic>), grid, block, lds, s, p);
+            launch_kernel((k_bwd_row<NV, U, WT, RES, WIDE, kModeAtomic, RC>), grid, block, lds, s, p);
         else
             return RMSN_ERR_SHAPE;
     } else if (rt.r.partial_f64) {
-        launch_kernel((k_bwd_row<NV, U, WT, RES, WIDE, kModePartF64>), grid, block, lds, s, p);
+        launch_kernel((k_bwd_row<NV, U, WT, RES, WIDE, kModePartF64, RC>), grid, block, lds, s, p);
     } else {
-        launch_kernel((k_bwd_row<NV, U, WT, RES, WIDE, kModePartF32>), grid, block, lds, s, p);
+        launch_kernel((k_bwd_row<NV, U, WT, RES, WIDE, kModePartF32, RC>), grid, block, lds, s, p);
     }
     return hipGetLastError() == hipSuccess ? RMSN_OK : RMSN_ERR_LAUNCH;
 }
 
-template <int NV, int U, typename WT, bool RES>
+template <int NV, int U, typename WT, bool RES, bool RC>
 static int launch_row_t(const BwdParams& p, const Route& rt, hipStream_t s) {
-    const size_t lds = bwd_row_lds_bytes(rt.r, p.H);
-    if (rt.r.lanes_per_row > 64) return launch_row_mode<NV, U, WT, RES, true>(p, rt, lds, s);
-    return launch_row_mode<NV, U, WT, RES, false>(p, rt, lds, s);
+    const size_t lds = bwd_row_lds_bytes(rt.r, p.H, RC);
+    if (rt.r.lanes_per_row > 64) return launch_row_mode<NV, U, WT, RES, true, RC>(p, rt, lds, s);
+    return launch_row_mode<NV, U, WT, RES, false, RC>(p, rt, lds, s);
 }
 
 // (NV, U) pairs compiled: NV * U <= 8, NV <= 2.
-template <typename WT, bool RES>
+template <typename WT, bool RES, bool RC>
 static int launch_row_shape(const BwdParams& p, const Route& rt, hipStream_t s) {
     const int nv = rt.r.vec_per_lane, u = rt.r.unroll;
     if (nv == 1) {
         switch (u) {
-            case 1: return launch_row_t<1, 1, WT, RES>(p, rt, s);
-            case 2: return launch_row_t<1, 2, WT, RES>(p, rt, s);
-            case 4: return launch_row_t<1, 4, WT, RES>(p, rt, s);
-            case 8: return launch_row_t<1, 8, WT, RES>(p, rt, s);
+            case 1: return launch_row_t<1, 1, WT, RES, RC>(p, rt, s);
+            case 2: return launch_row_t<1, 2, WT, RES, RC>(p, rt, s);
+            case 4: return launch_row_t<1, 4, WT, RES, RC>(p, rt, s);
+            case 8: return launch_row_t<1, 8, WT, RES, RC>(p, rt, s);
         }
     } else if (nv == 2) {
         switch (u) {
-            case 1: return launch_row_t<2, 1, WT, RES>(p, rt, s);
-            case 2: return launch_row_t<2, 2, WT, RES>(p, rt, s);
-            case 4: return launch_row_t<2, 4, WT, RES>(p, rt, s);
+            case 1: return launch_row_t<2, 1, WT, RES, RC>(p, rt, s);
+            case 2: return launch_row_t<2, 2, WT, RES, RC>(p, rt, s);
+            case 4: return launch_row_t<2, 4, WT, RES, RC>(p, rt, s);
         }
     }
     return RMSN_ERR_SHAPE;
@@ -487,9 +543,15 @@ static int launch_small_shape(const BwdParams& p, const Route& rt, hipStream_t s
     }
 }
 
+// form: kFormPlain, kFormResidual or kFormRecompute.
 template <typename WT>
-static int launch_bwd_row_wt(const BwdParams& p, const Route& rt, bool residual, hipStream_t s) {
-    return residual ? launch_row_shape<WT, true>(p, rt, s) : launch_row_shape<WT, false>(p, rt, s);
+static int launch_bwd_row_wt(const BwdParams& p, const Route& rt, int form, hipStream_t s) {
+    switch (form) {
+        case kFormPlain: return launch_row_shape<WT, false, false>(p, rt, s);
+        case kFormResidual: return launch_row_shape<WT, true, false>(p, rt, s);
+        case kFormRecompute: return launch_row_shape<WT, false, true>(p, rt, s);
+        default: return RMSN_ERR_SHAPE;
+    }
 }
 
 template <typename WT>

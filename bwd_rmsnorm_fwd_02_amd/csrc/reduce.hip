@@ -118,10 +118,10 @@ int launch_fwd(const FwdParams& p, const Route& rt, rmsn_dtype_t wdt, bool resid
     return wdt == RMSN_BF16 ? launch_fwd_bf16w(p, rt, residual, s) : launch_fwd_f32w(p, rt, residual, s);
 }
 
-int launch_bwd_row(const BwdParams& p, const Route& rt, rmsn_dtype_t wdt, bool residual,
+int launch_bwd_row(const BwdParams& p, const Route& rt, rmsn_dtype_t wdt, int form,
                    hipStream_t s) {
-    return wdt == RMSN_BF16 ? launch_bwd_row_bf16w(p, rt, residual, s)
-                            : launch_bwd_row_f32w(p, rt, residual, s);
+    return wdt == RMSN_BF16 ? launch_bwd_row_bf16w(p, rt, form, s)
+                            : launch_bwd_row_f32w(p, rt, form, s);
 }
 
 int launch_bwd_small(const BwdParams& p, const Route& rt, rmsn_dtype_t wdt, bool residual,

@@ -107,7 +107,9 @@ __device__ __forceinline__ void lds_barrier() {
 
 // Butterfly sum over aligned groups of G lanes (G a power of two <= 64);
 // every lane of the group receives the group's sum. The pairing order is
-// fixed, so the result is bit-reproducible.
+// fixed, so the result is bit-reproducible. The exchanges run through the
+// LDS crossbar (ds_bpermute), next to the vector ALU that the row
+// arithmetic keeps busy.
 template <int G>
 __device__ __forceinline__ float group_sum(float v) {
 #pragma unroll
@@ -130,6 +132,95 @@ __device__ __forceinline__ float group_sum_rt(float v, int g) {
 __device__ __forceinline__ double group_sum_rt(double v, int g) {
     for (int m = g >> 1; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
     return v;
+}
+
+// Lane exchanges on the vector ALU (no LDS): DPP quad permutes (partner
+// i^1, i^2), row rotations inside 16-lane rows, and the gfx950 permlane
+// swaps across 16-lane rows and 32-lane halves, where both partners receive
+// the lower and the upper lane's value.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp32(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, true);
+}
+
+template <int CTRL>
+__device__ __forceinline__ double dpp_partner(double v) {
+    const uint64_t u = (uint64_t)__double_as_longlong(v);
+    const uint64_t lo = dpp32<CTRL>((uint32_t)u), hi = dpp32<CTRL>((uint32_t)(u >> 32));
+    return __longlong_as_double((long long)((hi << 32) | lo));
+}
+
+// v(lower) + v(upper) over the lane pairs i, i ^ 16 (X = 16) or i, i ^ 32.
+template <int X>
+__device__ __forceinline__ double swap_sum(double v) {
+    const uint64_t u = (uint64_t)__double_as_longlong(v);
+    const uint32_t lo = (uint32_t)u, hi = (uint32_t)(u >> 32);
+    const auto rl = X == 16 ? __builtin_amdgcn_permlane16_swap(lo, lo, false, false)
+                            : __builtin_amdgcn_permlane32_swap(lo, lo, false, false);
+    const auto rh = X == 16 ? __builtin_amdgcn_permlane16_swap(hi, hi, false, false)
+                            : __builtin_amdgcn_permlane32_swap(hi, hi, false, false);
+    const double a = __longlong_as_double((long long)(((uint64_t)rh[0] << 32) | rl[0]));
+    const double b = __longlong_as_double((long long)(((uint64_t)rh[1] << 32) | rl[1]));
+    return a + b;
+}
+
+// FP64 sums over the 64 lanes of a wave of U per-lane values (U rows), for
+// rows that span whole waves, where only one lane per row needs the sum. The
+// first log2(U) stages scatter the rows: each lane keeps half of its rows,
+// adds its partner's values for them and hands over the other half (DPP
+// xor 1, xor 2, then, for U = 8, a row rotation by 4, whose source lane
+// always differs from the receiver in lane bit 2). Then each lane carries one
+// row: rotations by 4 and 8 inside 16-lane rows (they keep lane bits 0-1, so
+// the added values belong to the same row) and the two permlane swaps finish
+// the sum. Lane q < U returns the sum of row wave_row<U>(q). log2(U) + 4
+// exchanges instead of 6U; the order is fixed, so sums are reproducible.
+template <int N, int CTRL, typename T>
+__device__ __forceinline__ void scatter_stage(const T (&in)[2 * N], T (&out)[N], bool hi) {
+#pragma unroll
+    for (int j = 0; j < N; ++j) {
+        const T keep = hi ? in[N + j] : in[j];
+        const T give = hi ? in[j] : in[N + j];
+        out[j] = keep + dpp_partner<CTRL>(give);
+    }
+}
+
+template <int U, typename T>
+__device__ __forceinline__ T wave_sums(const T (&v)[U], int lane) {
+    static_assert(U == 1 || U == 2 || U == 4 || U == 8, "rows per wave sum");
+    T s;
+    if constexpr (U == 1) {
+        s = v[0] + dpp_partner<0xB1>(v[0]);
+        s = s + dpp_partner<0x4E>(s);
+    } else if constexpr (U == 2) {
+        T a[1];
+        scatter_stage<1, 0xB1>(v, a, lane & 1);
+        s = a[0] + dpp_partner<0x4E>(a[0]);
+    } else if constexpr (U == 4) {
+        T a[2], b[1];
+        scatter_stage<2, 0xB1>(v, a, lane & 1);
+        scatter_stage<1, 0x4E>(a, b, (lane >> 1) & 1);
+        s = b[0];
+    } else {
+        T a[4], b[2], c[1];
+        scatter_stage<4, 0xB1>(v, a, lane & 1);
+        scatter_stage<2, 0x4E>(a, b, (lane >> 1) & 1);
+        scatter_stage<1, 0x124>(b, c, (lane >> 2) & 1);
+        s = c[0];
+    }
+    if constexpr (U <= 4) s = s + dpp_partner<0x124>(s);  // row_ror:4
+    s = s + dpp_partner<0x128>(s);                        // row_ror:8
+    s = swap_sum<16>(s);
+    s = swap_sum<32>(s);
+    return s;
+}
+
+// The row whose sum wave_sums<U> leaves in lane q (q < U).
+template <int U>
+__device__ __forceinline__ int wave_row(int q) {
+    if constexpr (U == 1) return 0;
+    if constexpr (U == 2) return q & 1;
+    if constexpr (U == 4) return 2 * (q & 1) + ((q >> 1) & 1);
+    return 4 * (q & 1) + 2 * ((q >> 1) & 1) + ((q >> 2) & 1);
 }
 
 }  // namespace rmsn

@@ -18,6 +18,10 @@ constexpr int64_t kMaxH = 16384;
 // never from the device, so deterministic dw bits do not depend on the part.
 constexpr int kPartitionCUs = 256;
 
+// Backward forms: plain rows, fused residual (h, optional dres), or plain
+// rows with rstd recomputed from x inside the backward.
+enum { kFormPlain = 0, kFormResidual = 1, kFormRecompute = 2 };
+
 // Addressing of one tensor: row r = (t, head) starts at t*st_t + head*st_h.
 struct RowAddr {
     int64_t st_t;
@@ -61,6 +65,7 @@ struct BwdParams {
     int32_t rpb;
     int32_t ncol_blocks;    // column-task blocks (small-T kernel)
     int32_t col_splits;     // row splits per column task (small-T kernel)
+    float eps;              // recompute form only
 };
 
 struct Route {
@@ -68,9 +73,8 @@ struct Route {
     size_t workspace;       // bytes needed
 };
 
-// Route table (route.cpp). op 0 fwd, 1 bwd.
-int route(int op, int64_t rows, int64_t H, rmsn_dtype_t wdt, int det, int residual,
-          Route* out);
+// Route table (route.cpp). op 0 fwd, 1 bwd; form kForm* (backward).
+int route(int op, int64_t rows, int64_t H, rmsn_dtype_t wdt, int det, int form, Route* out);
 // Tuning override of the route table (NULL clears).
 int set_route_knobs(int op, const rmsn_route_knobs_t* knobs);
 
@@ -78,7 +82,7 @@ int set_route_knobs(int op, const rmsn_route_knobs_t* knobs);
 // hipGetLastError() mapped to an RMSN status.
 int launch_fwd(const FwdParams& p, const Route& rt, rmsn_dtype_t wdt, bool residual,
                hipStream_t s);
-int launch_bwd_row(const BwdParams& p, const Route& rt, rmsn_dtype_t wdt, bool residual,
+int launch_bwd_row(const BwdParams& p, const Route& rt, rmsn_dtype_t wdt, int form,
                    hipStream_t s);
 int launch_dw_reduce(const BwdParams& p, const Route& rt, hipStream_t s);
 int launch_bwd_small(const BwdParams& p, const Route& rt, rmsn_dtype_t wdt, bool residual,
@@ -87,8 +91,8 @@ int launch_fill_zero(void* ptr, size_t bytes, hipStream_t s);
 // Per weight dtype (one translation unit each, compiled in parallel).
 int launch_fwd_bf16w(const FwdParams& p, const Route& rt, bool residual, hipStream_t s);
 int launch_fwd_f32w(const FwdParams& p, const Route& rt, bool residual, hipStream_t s);
-int launch_bwd_row_bf16w(const BwdParams& p, const Route& rt, bool residual, hipStream_t s);
-int launch_bwd_row_f32w(const BwdParams& p, const Route& rt, bool residual, hipStream_t s);
+int launch_bwd_row_bf16w(const BwdParams& p, const Route& rt, int form, hipStream_t s);
+int launch_bwd_row_f32w(const BwdParams& p, const Route& rt, int form, hipStream_t s);
 int launch_bwd_small_bf16w(const BwdParams& p, const Route& rt, bool residual, hipStream_t s);
 int launch_bwd_small_f32w(const BwdParams& p, const Route& rt, bool residual, hipStream_t s);
 

@@ -153,15 +153,14 @@ int set_route_knobs(int op, const rmsn_route_knobs_t* k) {
     return RMSN_OK;
 }
 
-int route(int op, int64_t rows, int64_t H, rmsn_dtype_t wdt, int det, int residual,
-          Route* out) {
+int route(int op, int64_t rows, int64_t H, rmsn_dtype_t wdt, int det, int form, Route* out) {
     if (!out) return RMSN_ERR_NULL;
     memset(out, 0, sizeof(*out));
     if (wdt != RMSN_BF16 && wdt != RMSN_F32) return RMSN_ERR_DTYPE;
     if (H < kVec || H > kMaxH || H % kVec != 0 || rows < 0 || rows > INT32_MAX)
         return RMSN_ERR_SHAPE;
     if (op != 0 && op != 1) return RMSN_ERR_SHAPE;
-    (void)residual;
+    if (form != kFormPlain && form != kFormResidual && form != kFormRecompute) return RMSN_ERR_SHAPE;
     const int nvec = (int)(H / kVec);
     rmsn_route_t& r = out->r;
     int st;
@@ -179,8 +178,10 @@ int route(int op, int64_t rows, int64_t H, rmsn_dtype_t wdt, int det, int residu
         return RMSN_OK;
     }
 
-    if (rows <= kSmallRows) {
+    if (rows <= kSmallRows && form != kFormRecompute) {
         // Column tasks for dw + row tasks for dx in one launch of 256 threads.
+        // (The recompute form takes the row kernel at every T: its column
+        // tasks would need every row's rstd before they start.)
         const int nv = nvec <= 256 ? 1 : (nvec <= 512 ? 2 : (nvec <= 1024 ? 4 : 8));
         const int tpr = lanes_per_row(nvec, nv);
         const int rpb = tpr <= 256 ? 256 / tpr : 1;

@@ -102,8 +102,9 @@ int rmsnorm_residual_fwd(const void* x, const void* r, const void* w,
 
 /* --------------------------------------------------------------- backward */
 
-/* Bytes of workspace the backward needs for this shape and mode (0 when the
- * chosen kernels need none; callers may still pass a larger buffer). */
+/* Bytes of workspace the backward needs for this shape and mode, enough for
+ * every backward entry point below (0 when none of their kernels needs any;
+ * callers may still pass a larger buffer). */
 size_t rmsnorm_bwd_workspace_bytes(int64_t rows, int64_t H, rmsn_dtype_t w_dtype,
                                    int deterministic);
 
@@ -129,6 +130,26 @@ int rmsnorm_bwd_strided(const void* dy, rmsn_view_t dyv, const void* x, rmsn_vie
                         const float* rstd, const void* w, rmsn_dtype_t w_dtype,
                         int deterministic, void* dx, rmsn_view_t dxv, float* dw,
                         void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Backward that takes no rstd: each row's rstd is recomputed from x inside
+ * the backward kernel, while the row is in registers, with the forward's own
+ * arithmetic (FP32 sums of squares over 8-element groups, added in FP64,
+ * 1/sqrt(mean + eps) in FP64 rounded once to FP32). For activation
+ * recompute: the pages time a checkpointed training step as forward,
+ * forward recompute, backward ("2xfwd+bwd", flashinfer PR #8827 "Key"); a
+ * caller that kept x and needs no second y can replace the recompute
+ * forward and the backward with this one call, saving the recompute's
+ * read of x and write of y. The recomputed rstd equals the forward's
+ * whenever the FP64 sum of a row's FP32 group sums is exact in both
+ * summation orders, which holds unless those group sums span more than
+ * 2^(29 - log2(H/8)) in magnitude; otherwise it can differ in the last bit.
+ * Views, outputs, modes and workspace as in rmsnorm_bwd_strided; eps as
+ * in the forward (RMSN_ERR_EPS if negative or not finite). At every T this
+ * runs the row kernel (no small-T column-task kernel). */
+int rmsnorm_bwd_recompute(const void* dy, rmsn_view_t dyv, const void* x, rmsn_view_t xv,
+                          const void* w, rmsn_dtype_t w_dtype, float eps, int deterministic,
+                          void* dx, rmsn_view_t dxv, float* dw, void* workspace,
+                          size_t workspace_bytes, hipStream_t stream);
 
 /* Residual backward on contiguous [T, H]: h is the forward's BF16 h_new;
  * dres (nullable) is the gradient arriving at h_new from the residual
@@ -168,10 +189,13 @@ typedef struct {
 } rmsn_route_t;
 
 /* The route table: which kernel and launch shape serve this problem.
- * op: 0 forward, 1 backward. Pure host function; needs no GPU.
+ * op: 0 forward, 1 backward. form (backward only; ignored for the forward):
+ * 0 plain (rmsnorm_bwd, rmsnorm_bwd_strided), 1 residual
+ * (rmsnorm_residual_bwd), 2 recompute (rmsnorm_bwd_recompute).
+ * Pure host function; needs no GPU.
  * Returns RMSN_OK or RMSN_ERR_SHAPE / RMSN_ERR_DTYPE / RMSN_ERR_NULL. */
 int rmsnorm_route_query(int op, int64_t rows, int64_t H, rmsn_dtype_t w_dtype,
-                        int deterministic, int residual, rmsn_route_t* out);
+                        int deterministic, int form, rmsn_route_t* out);
 
 /* Launch-shape knobs for benchmarks and tuning sweeps (not part of the
  * method). A zero field keeps the table's choice. The route is still derived

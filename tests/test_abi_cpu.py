@@ -120,6 +120,30 @@ def test_bwd_argument_errors():
     assert f(_fake(DY), _fake(X), _fake(RS), _fake(W + 4), 1, 1, _fake(DX), _fake(DW), T, H, _fake(WS), need, s) == -4
 
 
+@fake_only
+def test_bwd_recompute_argument_errors():
+    A = 0x40000000
+    s = P(0)
+    V = _lib.View
+    f = lib.rmsnorm_bwd_recompute
+    T, H = 4096, 2048
+    v = V(T, 1, H, H, 0)
+    DY, X, W, DX, DW, WS = (A + i * 0x4000000 for i in range(6))
+    need = lib.rmsnorm_bwd_workspace_bytes(T, H, 1, 1)
+    args = lambda **k: [_fake(k.get("dy", DY)), v, _fake(k.get("x", X)) if k.get("x", X) else None, v,
+                        _fake(W), 1, k.get("eps", 1e-6), 1, _fake(k.get("dx", DX)), v, _fake(DW),
+                        _fake(WS), k.get("ws", need), s]
+    assert f(*args(eps=-1.0)) == -9
+    assert f(*args(eps=float("nan"))) == -9
+    assert f(*args(eps=float("inf"))) == -9
+    assert f(*args(x=0)) == -1
+    assert f(*args(dx=X)) == -7          # dx over x
+    assert f(*args(ws=need - 1)) == -5
+    # views must agree
+    assert f(_fake(DY), v, _fake(X), V(T, 1, H + 8, H + 8, 0), _fake(W), 1, 1e-6, 1, _fake(DX), v,
+             _fake(DW), _fake(WS), need, s) == -3
+
+
 # ------------------------------------------------------------------ routes
 
 def route(op, rows, H, wdt=0, det=1, res=0):
@@ -137,7 +161,25 @@ def test_route_small_t_uses_column_tasks_in_both_modes():
         # above the column-task window both modes run the two-stage path by
         # default (the atomic finalise measured slower on MI355X)
         assert r.kind == _lib.RMSN_KIND_BWD_ROW_DET
-    assert lib.rmsnorm_bwd_workspace_bytes(64, 256, 1, 1) == 0
+
+
+def test_route_recompute_form_runs_the_row_kernel_at_every_t():
+    for det in (0, 1):
+        for rows in (1, 2, 64, 65, 4096, 131072):
+            st, r = route(1, rows, 256, 1, det, 2)
+            assert st == 0 and r.kind == _lib.RMSN_KIND_BWD_ROW_DET
+            _, plain = route(1, rows, 256, 1, det, 0)
+            if rows > 64:
+                # above the column-task window both forms share one launch shape
+                # and partition, so their dx and dw bits agree for equal rstd
+                for f in ("grid", "vec_per_lane", "lanes_per_row", "rows_per_block", "unroll",
+                          "partials", "partial_f64"):
+                    assert getattr(r, f) == getattr(plain, f), f
+    # the workspace query covers the recompute form's partials at small T
+    _, r = route(1, 64, 256, 1, 1, 2)
+    assert r.partials >= 1
+    assert lib.rmsnorm_bwd_workspace_bytes(64, 256, 1, 1) >= r.partials * 256 * 4
+    assert route(1, 100, 256, 0, 1, 3)[0] == -3  # no such form
 
 
 def test_route_deterministic_partition_is_a_function_of_shape():
