@@ -46,8 +46,9 @@ int lanes_per_row(int nvec, int nv) {
 size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
 
 // Default launch shapes of the row kernels by width (nvec 16-byte vectors
-// per row), chosen by timing every compiled shape on MI355X at the quoted
-// workloads: H 256 (per-head views), 2048, 4096 and 6144 (residual).
+// per row), chosen by timing every compiled shape on MI355X in step mode
+// (forward then backward, as training runs them) at H 256 (per-head views),
+// 512, 1536, 2048, 4096, 5120, 6144 (residual) and 8192.
 // rpb_threads sets the row groups per block (threads / lanes per row).
 struct Shape {
     int nv, unroll, rpb, bpc;
@@ -57,16 +58,24 @@ struct Entry {
 };
 constexpr Entry kFwdTable[] = {
     {32, 4, 1, 256, 2},     // H <= 256: 8 lanes per row, 32 rows per block
+    {64, 4, 1, 256, 2},     // H <= 512: 16 lanes per row, 16 rows per block
+    {192, 2, 1, 1024, 1},   // H <= 1536: up to 128 lanes per row, 1024-thread blocks
     {256, 2, 1, 512, 1},    // H <= 2048
     {512, 2, 4, 256, 4},    // H <= 4096: 256 lanes per row, 4 rows per iteration
-    {1024, 2, 1, 0, 1},     // H <= 8192
+    {640, 2, 1, 0, 2},      // H <= 5120: one row per block, 2 blocks per CU
+    {768, 2, 1, 0, 1},      // H <= 6144
+    {1024, 2, 1, 0, 2},     // H <= 8192
     {1 << 30, 4, 1, 0, 1},  // H <= 16384
 };
 constexpr Entry kBwdTable[] = {
     {32, 2, 1, 128, 4},     // H <= 256: 16 lanes per row, 8 rows per block, 4 blocks per CU
+    {64, 2, 1, 128, 4},     // H <= 512: 32 lanes per row, 4 rows per block, 4 blocks per CU
+    {192, 1, 1, 768, 1},    // H <= 1536: one lane per vector, 768-thread blocks
     {256, 1, 2, 512, 1},    // H <= 2048: 2 row groups of up to 256 lanes, 1 block per CU
     {512, 1, 1, 0, 2},      // H <= 4096: one row per block, 2 blocks per CU
-    {1024, 2, 2, 0, 1},     // H <= 8192
+    {640, 1, 1, 0, 1},      // H <= 5120: one lane per vector, one row per block
+    {768, 2, 2, 0, 1},      // H <= 6144
+    {1024, 1, 1, 0, 1},     // H <= 8192: 1024 lanes, one row per block
     {1 << 30, 2, 1, 0, 1},  // H <= 16384
 };
 

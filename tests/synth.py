@@ -156,7 +156,16 @@ CONFIGS = {
 }
 
 
+# The other widths of the pages' seven (256, 512, 1536, 2048, 4096, 5120,
+# 6144), at large token counts (their top windows run up to T 1,048,576).
+WIDTH_CONFIGS = {
+    "w512_T1048576_bf16w": dict(T=1048576, H=512, w_dtype="bf16"),
+    "w1536_T262144_f32w": dict(T=262144, H=1536, w_dtype="f32"),
+    "w5120_T65536_bf16w": dict(T=65536, H=5120, w_dtype="bf16"),
+}
+
+
 def config(name: str, seed: int = 0, **overrides) -> Workload:
-    kw = dict(CONFIGS[name])
+    kw = dict(CONFIGS[name] if name in CONFIGS else WIDTH_CONFIGS[name])
     kw.update(overrides)
     return make(seed=seed, name=name, **kw)

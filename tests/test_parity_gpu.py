@@ -222,7 +222,7 @@ def _sample_rows(rows: int, extra=None, k: int = 48, seed: int = 123) -> np.ndar
     return np.array(sorted(pick))
 
 
-@pytest.mark.parametrize("name", list(synth.CONFIGS))
+@pytest.mark.parametrize("name", list(synth.CONFIGS) + list(synth.WIDTH_CONFIGS))
 def test_full_size_config(name):
     _announce(f"full-size {name}: generating")
     wl = synth.config(name, seed=0)
