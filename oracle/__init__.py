@@ -11,6 +11,12 @@ backward routes", opening description and "Key"/"Workload" paragraphs):
 * ``fwd``: rstd = 1/sqrt(mean(x^2) + eps), y = x*rstd*w
 * ``bwd``: dx = rstd*(dy*w - xhat*c), c = mean(dy*w*xhat), dw = sum_t dy*xhat
 * ``residual_add``: h = BF16(x + r)
+* ``ln_fwd`` / ``ln_bwd``: LayerNorm, the adjacent normalisation of the same
+  benchmark suite (ROCm TransformerEngine PR "Microbenchmarking and CI
+  performance regression test", benchmark_normalization): mu = mean(x),
+  var = mean((x - mu)^2), rstd = 1/sqrt(var + eps),
+  y = (x - mu)*rstd*gamma + beta; dx = rstd*(g - mean(g) - xhat*mean(g*xhat))
+  with g = dy*gamma, dgamma = sum_t dy*xhat, dbeta = sum_t dy
 
 Inputs are BF16 bit patterns (numpy ``uint16``) for x, dy, r, and float64 for
 w and rstd. All arrays are contiguous ``[rows, H]``; per-head views are
@@ -59,9 +65,14 @@ def _load():
     lib.orc_residual_add.argtypes = [i64, p, p, p]
     lib.orc_fwd_f64.argtypes = [i64, i64, p, p, ctypes.c_double, p, p]
     lib.orc_bwd_f64.argtypes = [i64, i64, p, p, p, p, p, p, p]
+    lib.orc_ln_fwd.argtypes = [i64, i64, p, p, p, ctypes.c_double, p, p, p]
+    lib.orc_ln_bwd.argtypes = [i64, i64, p, p, p, p, p, p, p, p, p]
+    lib.orc_ln_fwd_f64.argtypes = [i64, i64, p, p, p, ctypes.c_double, p, p, p]
+    lib.orc_ln_bwd_f64.argtypes = [i64, i64, p, p, p, p, p, p, p, p, p]
     for f in (lib.orc_bf16_to_double, lib.orc_round_bf16, lib.orc_round_f32,
               lib.orc_fwd, lib.orc_bwd, lib.orc_residual_add,
-              lib.orc_fwd_f64, lib.orc_bwd_f64):
+              lib.orc_fwd_f64, lib.orc_bwd_f64, lib.orc_ln_fwd, lib.orc_ln_bwd,
+              lib.orc_ln_fwd_f64, lib.orc_ln_bwd_f64):
         f.restype = None
     _lib = lib
     return lib
@@ -162,3 +173,80 @@ def residual_add(x_bits: np.ndarray, r_bits: np.ndarray) -> np.ndarray:
     h = np.empty(x_bits.shape, np.uint16)
     _load().orc_residual_add(x_bits.size, _ptr(x_bits), _ptr(r_bits), _ptr(h))
     return h
+
+
+# ------------------------------------------------------------------ LayerNorm
+
+def _ln_params(H, gamma, beta):
+    gamma = _c(gamma, np.float64)
+    assert gamma.shape == (H,)
+    if beta is not None:
+        beta = _c(beta, np.float64)
+        assert beta.shape == (H,)
+    return gamma, beta
+
+
+def ln_fwd(x_bits: np.ndarray, gamma: np.ndarray, beta, eps: float, want_y: bool = True):
+    """LayerNorm forward over rows of x (BF16 bits). beta may be None (zero).
+    Returns (mu[rows], rstd[rows], y[rows, H] or None), float64."""
+    x_bits = _c(x_bits, np.uint16)
+    rows, H = x_bits.shape
+    gamma, beta = _ln_params(H, gamma, beta)
+    mu = np.empty(rows, np.float64)
+    rstd = np.empty(rows, np.float64)
+    y = np.empty((rows, H), np.float64) if want_y else None
+    _load().orc_ln_fwd(rows, H, _ptr(x_bits), _ptr(gamma), _ptr(beta), float(eps),
+                       _ptr(mu), _ptr(rstd), _ptr(y))
+    return mu, rstd, y
+
+
+def ln_bwd(dy_bits: np.ndarray, x_bits: np.ndarray, mu: np.ndarray, rstd: np.ndarray,
+           gamma: np.ndarray, want_dx: bool = True):
+    """LayerNorm backward at the given mu and rstd. Returns
+    (dx or None, c[rows, 2] = (c1, c2) or None, dgamma, dbeta), float64."""
+    dy_bits = _c(dy_bits, np.uint16)
+    x_bits = _c(x_bits, np.uint16)
+    rows, H = x_bits.shape
+    assert dy_bits.shape == (rows, H)
+    mu = _c(mu, np.float64)
+    rstd = _c(rstd, np.float64)
+    assert mu.shape == (rows,) and rstd.shape == (rows,)
+    gamma, _ = _ln_params(H, gamma, None)
+    dx = np.empty((rows, H), np.float64) if want_dx else None
+    c = np.empty((rows, 2), np.float64) if want_dx else None
+    dg = np.empty(H, np.float64)
+    db = np.empty(H, np.float64)
+    _load().orc_ln_bwd(rows, H, _ptr(dy_bits), _ptr(x_bits), _ptr(mu), _ptr(rstd), _ptr(gamma),
+                       _ptr(dx), _ptr(c), _ptr(dg), _ptr(db))
+    return dx, c, dg, db
+
+
+def ln_fwd_f64(x: np.ndarray, gamma: np.ndarray, beta, eps: float):
+    """LayerNorm forward on unrounded float64 rows (same per-row code)."""
+    x = _c(x, np.float64)
+    rows, H = x.shape
+    gamma, beta = _ln_params(H, gamma, beta)
+    mu = np.empty(rows, np.float64)
+    rstd = np.empty(rows, np.float64)
+    y = np.empty((rows, H), np.float64)
+    _load().orc_ln_fwd_f64(rows, H, _ptr(x), _ptr(gamma), _ptr(beta), float(eps),
+                           _ptr(mu), _ptr(rstd), _ptr(y))
+    return mu, rstd, y
+
+
+def ln_bwd_f64(dy: np.ndarray, x: np.ndarray, mu: np.ndarray, rstd: np.ndarray,
+               gamma: np.ndarray):
+    """LayerNorm backward on unrounded float64 rows (same per-row code)."""
+    dy = _c(dy, np.float64)
+    x = _c(x, np.float64)
+    rows, H = x.shape
+    mu = _c(mu, np.float64)
+    rstd = _c(rstd, np.float64)
+    gamma, _ = _ln_params(H, gamma, None)
+    dx = np.empty((rows, H), np.float64)
+    c = np.empty((rows, 2), np.float64)
+    dg = np.empty(H, np.float64)
+    db = np.empty(H, np.float64)
+    _load().orc_ln_bwd_f64(rows, H, _ptr(dy), _ptr(x), _ptr(mu), _ptr(rstd), _ptr(gamma),
+                           _ptr(dx), _ptr(c), _ptr(dg), _ptr(db))
+    return dx, c, dg, db

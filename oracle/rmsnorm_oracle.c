@@ -212,3 +212,132 @@ void orc_residual_add(int64_t n, const uint16_t* x, const uint16_t* r,
         h_out[i] = double_to_bf16_bits(s);
     }
 }
+
+/* ------------------------------------------------------------ LayerNorm
+ *
+ * The adjacent normalisation in the same training stacks (ROCm
+ * TransformerEngine PR "Microbenchmarking and CI performance regression
+ * test", benchmark_normalization table: RMSNorm and LayerNorm forward and
+ * backward on MI355). The usual definition, per row:
+ *
+ *   forward   mu = (1/H) sum_j x_j,  var = (1/H) sum_j (x_j - mu)^2,
+ *             rstd = 1/sqrt(var + eps),  xhat = (x - mu) * rstd,
+ *             y = xhat * gamma + beta
+ *   backward  g = dy * gamma,  c1 = (1/H) sum_j g_j,
+ *             c2 = (1/H) sum_j g_j * xhat_j,
+ *             dx = rstd * (g - c1 - xhat * c2)
+ *             dgamma_j = sum_t dy_tj * xhat_tj,  dbeta_j = sum_t dy_tj
+ *
+ * The variance is the two-pass one (deviations from the mean), as a plain
+ * reading of the definition.
+ */
+
+static void ln_row_fwd(int64_t H, const double* x, const double* gamma, const double* beta,
+                       double eps, double* mu_out, double* rstd_out, double* y) {
+    nsum_t s = {0.0, 0.0};
+    for (int64_t j = 0; j < H; ++j) nsum_add(&s, x[j]);
+    double mu = nsum_value(&s) / (double)H;
+    nsum_t v = {0.0, 0.0};
+    for (int64_t j = 0; j < H; ++j) nsum_add(&v, (x[j] - mu) * (x[j] - mu));
+    double var = nsum_value(&v) / (double)H;
+    double rstd = 1.0 / sqrt(var + eps);
+    *mu_out = mu;
+    *rstd_out = rstd;
+    if (y) {
+        for (int64_t j = 0; j < H; ++j) {
+            double xhat = (x[j] - mu) * rstd;
+            y[j] = xhat * gamma[j] + (beta ? beta[j] : 0.0);
+        }
+    }
+}
+
+static void ln_row_bwd(int64_t H, const double* dy, const double* x, double mu, double rstd,
+                       const double* gamma, double* dx, double* c_out, nsum_t* dg_acc,
+                       nsum_t* db_acc) {
+    if (dx || c_out) {
+        nsum_t s1 = {0.0, 0.0}, s2 = {0.0, 0.0};
+        for (int64_t j = 0; j < H; ++j) {
+            double xhat = (x[j] - mu) * rstd;
+            double g = dy[j] * gamma[j];
+            nsum_add(&s1, g);
+            nsum_add(&s2, g * xhat);
+        }
+        double c1 = nsum_value(&s1) / (double)H;
+        double c2 = nsum_value(&s2) / (double)H;
+        if (c_out) {
+            c_out[0] = c1;
+            c_out[1] = c2;
+        }
+        if (dx) {
+            for (int64_t j = 0; j < H; ++j) {
+                double xhat = (x[j] - mu) * rstd;
+                double g = dy[j] * gamma[j];
+                dx[j] = rstd * (g - c1 - xhat * c2);
+            }
+        }
+    }
+    for (int64_t j = 0; j < H; ++j) {
+        double xhat = (x[j] - mu) * rstd;
+        nsum_add(&dg_acc[j], dy[j] * xhat);
+        nsum_add(&db_acc[j], dy[j]);
+    }
+}
+
+void orc_ln_fwd_f64(int64_t rows, int64_t H, const double* x, const double* gamma,
+                    const double* beta, double eps, double* mu_out, double* rstd_out,
+                    double* y_out) {
+    for (int64_t t = 0; t < rows; ++t)
+        ln_row_fwd(H, x + t * H, gamma, beta, eps, mu_out + t, rstd_out + t,
+                   y_out ? y_out + t * H : NULL);
+}
+
+void orc_ln_bwd_f64(int64_t rows, int64_t H, const double* dy, const double* x,
+                    const double* mu, const double* rstd, const double* gamma, double* dx_out,
+                    double* c_out, double* dgamma_out, double* dbeta_out) {
+    nsum_t* dg = (nsum_t*)xalloc((size_t)H, sizeof(nsum_t));
+    nsum_t* db = (nsum_t*)xalloc((size_t)H, sizeof(nsum_t));
+    for (int64_t t = 0; t < rows; ++t)
+        ln_row_bwd(H, dy + t * H, x + t * H, mu[t], rstd[t], gamma,
+                   dx_out ? dx_out + t * H : NULL, c_out ? c_out + 2 * t : NULL, dg, db);
+    for (int64_t j = 0; j < H; ++j) {
+        dgamma_out[j] = nsum_value(&dg[j]);
+        dbeta_out[j] = nsum_value(&db[j]);
+    }
+    free(db);
+    free(dg);
+}
+
+void orc_ln_fwd(int64_t rows, int64_t H, const uint16_t* x, const double* gamma,
+                const double* beta, double eps, double* mu_out, double* rstd_out,
+                double* y_out) {
+    double* xr = (double*)xalloc((size_t)H, sizeof(double));
+    for (int64_t t = 0; t < rows; ++t) {
+        orc_bf16_to_double(H, x + t * H, xr);
+        ln_row_fwd(H, xr, gamma, beta, eps, mu_out + t, rstd_out + t,
+                   y_out ? y_out + t * H : NULL);
+    }
+    free(xr);
+}
+
+void orc_ln_bwd(int64_t rows, int64_t H, const uint16_t* dy, const uint16_t* x,
+                const double* mu, const double* rstd, const double* gamma, double* dx_out,
+                double* c_out, double* dgamma_out, double* dbeta_out) {
+    nsum_t* dg = (nsum_t*)xalloc((size_t)H, sizeof(nsum_t));
+    nsum_t* db = (nsum_t*)xalloc((size_t)H, sizeof(nsum_t));
+    double* xr = (double*)xalloc((size_t)H, sizeof(double));
+    double* dyr = (double*)xalloc((size_t)H, sizeof(double));
+    for (int64_t t = 0; t < rows; ++t) {
+        orc_bf16_to_double(H, x + t * H, xr);
+        orc_bf16_to_double(H, dy + t * H, dyr);
+        ln_row_bwd(H, dyr, xr, mu[t], rstd[t], gamma, dx_out ? dx_out + t * H : NULL,
+                   c_out ? c_out + 2 * t : NULL, dg, db);
+    }
+    for (int64_t j = 0; j < H; ++j) {
+        dgamma_out[j] = nsum_value(&dg[j]);
+        dbeta_out[j] = nsum_value(&db[j]);
+    }
+    free(dyr);
+    free(xr);
+    free(db);
+    free(dg);
+}

@@ -62,6 +62,28 @@ void orc_bwd_f64(int64_t rows, int64_t H, const double* dy, const double* x,
 void orc_residual_add(int64_t n, const uint16_t* x, const uint16_t* r,
                       uint16_t* h_out);
 
+/* LayerNorm (the adjacent normalisation of the same benchmark suite: ROCm
+ * TransformerEngine PR "Microbenchmarking and CI performance regression
+ * test", benchmark_normalization). Forward per row: mu = mean(x),
+ * var = mean((x - mu)^2), rstd = 1/sqrt(var + eps),
+ * y = (x - mu)*rstd*gamma + beta (beta may be NULL: zero). */
+void orc_ln_fwd(int64_t rows, int64_t H, const uint16_t* x, const double* gamma,
+                const double* beta, double eps, double* mu_out, double* rstd_out,
+                double* y_out);
+/* Backward at given mu and rstd: xhat = (x - mu)*rstd, g = dy*gamma,
+ * c1 = mean(g), c2 = mean(g*xhat), dx = rstd*(g - c1 - xhat*c2);
+ * dgamma_j = sum_t dy*xhat, dbeta_j = sum_t dy. c_out (nullable) receives
+ * [c1, c2] per row; dx_out may be NULL. */
+void orc_ln_bwd(int64_t rows, int64_t H, const uint16_t* dy, const uint16_t* x,
+                const double* mu, const double* rstd, const double* gamma, double* dx_out,
+                double* c_out, double* dgamma_out, double* dbeta_out);
+void orc_ln_fwd_f64(int64_t rows, int64_t H, const double* x, const double* gamma,
+                    const double* beta, double eps, double* mu_out, double* rstd_out,
+                    double* y_out);
+void orc_ln_bwd_f64(int64_t rows, int64_t H, const double* dy, const double* x,
+                    const double* mu, const double* rstd, const double* gamma, double* dx_out,
+                    double* c_out, double* dgamma_out, double* dbeta_out);
+
 #ifdef __cplusplus
 }
 #endif

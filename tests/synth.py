@@ -169,3 +169,55 @@ def config(name: str, seed: int = 0, **overrides) -> Workload:
     kw = dict(CONFIGS[name] if name in CONFIGS else WIDTH_CONFIGS[name])
     kw.update(overrides)
     return make(seed=seed, name=name, **kw)
+
+
+# ------------------------------------------------------------------ LayerNorm
+
+@dataclasses.dataclass
+class LNWorkload:
+    """One seeded LayerNorm problem: x, dy BF16 bits [T, H]; gamma, beta in
+    the weight dtype."""
+    name: str
+    T: int
+    H: int
+    gamma: Weight
+    beta: Weight
+    x: np.ndarray
+    dy: np.ndarray
+    eps: float = 1e-5
+
+
+def make_ln(T: int, H: int, w_dtype: str, seed: int, *, offset: float = 0.0,
+            name: str = "") -> LNWorkload:
+    """x = N(0,1) + offset and dy = N(0,1), drawn in float32 and rounded to
+    BF16; gamma = 1 + 0.1 N(0,1) and beta = 0.1 N(0,1) in the weight dtype.
+    Draw order: gamma, beta, x, dy. A nonzero offset stresses the mean
+    subtraction (|mu| well above the spread of a row)."""
+    rng = np.random.default_rng(seed)
+    gamma = weight(rng, H, w_dtype)
+    b32 = (0.1 * rng.standard_normal(H, dtype=np.float32)).astype(np.float32)
+    if w_dtype == "bf16":
+        bb = bf16_bits(b32)
+        beta = Weight("bf16", bb, bits_to_f32(bb))
+    else:
+        beta = Weight("f32", None, b32)
+    x = bf16_bits(rng.standard_normal((T, H), dtype=np.float32) + np.float32(offset))
+    dy = normal_bf16(rng, (T, H))
+    return LNWorkload(name=name, T=T, H=H, gamma=gamma, beta=beta, x=x, dy=dy)
+
+
+# LayerNorm workloads: the shapes of the benchmark_normalization table of
+# ROCm TransformerEngine PR "Microbenchmarking and CI performance regression
+# test" (M tokens x hidden, BF16), largest M.
+LN_CONFIGS = {
+    "ln_T8192_H4096_bf16w": dict(T=8192, H=4096, w_dtype="bf16"),
+    "ln_T8192_H8192_bf16w": dict(T=8192, H=8192, w_dtype="bf16"),
+    "ln_T8192_H3584_bf16w": dict(T=8192, H=3584, w_dtype="bf16"),
+    "ln_T8192_H16384_bf16w": dict(T=8192, H=16384, w_dtype="bf16"),
+}
+
+
+def ln_config(name: str, seed: int = 0, **overrides) -> LNWorkload:
+    kw = dict(LN_CONFIGS[name])
+    kw.update(overrides)
+    return make_ln(seed=seed, name=name, **kw)
