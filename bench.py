@@ -9,6 +9,12 @@ synthetic tensors already resident in HBM. Consecutive steps rotate over
 enough buffer sets (>= 1 GiB in the cycle) that no step finds its tensors in
 the 256 MB Infinity Cache, so the figure is an HBM figure.
 
+--norm layernorm times LayerNorm instead (the other normalisation of the
+benchmark_normalization table on the TE page; its workloads are named
+ln_T<tokens>_H<hidden>_<weight dtype>, default ln_T8192_H4096_bf16w): a step
+is its forward (y, mean, rstd) and deterministic backward (dx, dgamma,
+dbeta); ops fwd+bwd, fwd, bwd and 2xfwd+bwd.
+
 --op picks what a step is (the pages time fwd, bwd and "2xfwd+bwd", the
 checkpointed step: forward, forward recompute, backward):
   fwd+bwd (default)    forward, backward
@@ -51,6 +57,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBPS = 8000.0
 METRIC = "RMSNorm fwd+bwd effective HBM GB/s and % of 8 TB/s peak, per (T,H)"
 DEFAULT_CONFIG = "c2_T4096_H4096_bf16w"
+DEFAULT_LN_CONFIG = "ln_T8192_H4096_bf16w"
 OPS = ("fwd+bwd", "fwd", "bwd", "2xfwd+bwd", "fwd+bwd_recompute")
 
 
@@ -63,151 +70,22 @@ def algorithmic_bytes(rows: int, H: int, sw: int, residual: bool, with_dres: boo
     return fwd, bwd_row, bwd
 
 
-def main() -> int:
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=400)
-    ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--config", default=DEFAULT_CONFIG)
-    ap.add_argument("--op", choices=OPS, default="fwd+bwd")
-    ap.add_argument("--replays", type=int, default=5)
-    ap.add_argument("--seed", type=int, default=0)
-    ap.add_argument("--cpu-seconds", type=float, default=10.0,
-                    help="seconds of oracle work for each of the two CPU runs")
-    ap.add_argument("--cpu-threads", type=int, default=0,
-                    help="host threads for the oracle run (0: min(16, CPUs))")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
-                    help="only run a plain device copy of BYTES bytes 10 times (the reference "
-                         "kernel for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE) and exit")
-    args = ap.parse_args()
+def ln_algorithmic_bytes(rows: int, H: int, sw: int):
+    """LayerNorm bytes per launch: forward reads x, gamma, beta and writes y,
+    mean, rstd; the backward row kernel reads dy, x, mean, rstd, gamma and
+    writes dx; the reduce writes dgamma and dbeta."""
+    e = rows * H
+    fwd = 4 * e + 8 * rows + 2 * H * sw
+    bwd_row = 6 * e + 8 * rows + H * sw
+    return fwd, bwd_row, bwd_row + 8 * H
 
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU only: this RMSNorm path has no multi-GPU step "
-              "(rows shard across GPUs with no exchange but one dw all-reduce, which is "
-              "not built); run with --gpus 1.", file=sys.stderr)
-        return 2
 
-    import numpy as np
-    import torch
-
-    import bwd_rmsnorm_fwd_02_amd as rn
-    from bwd_rmsnorm_fwd_02_amd import _lib
-    from tests import synth
-
-    lib = _lib.load()  # raises if the HIP library is missing: no fallback
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-
-    if args.copy_calibration:
-        n = args.copy_calibration // 2
-        src = torch.ones(n, dtype=torch.bfloat16, device=dev)
-        dst = torch.empty_like(src)
-        for _ in range(10):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        print(json.dumps({"copy_calibration_bytes": n * 2, "launches": 10}), flush=True)
-        return 0
-
-    wl = synth.config(args.config, seed=args.seed)
-    rows, H, T, heads = wl.rows, wl.H, wl.T, wl.heads
-    residual = wl.r is not None
-    with_dres = wl.dres is not None
-    sw = 2 if wl.w.dtype == "bf16" else 4
-    wdt = _lib.RMSN_BF16 if wl.w.dtype == "bf16" else _lib.RMSN_F32
-    fwd_b, bwd_row_b, bwd_b = algorithmic_bytes(rows, H, sw, residual, with_dres)
-    op = args.op
-    rc = op == "fwd+bwd_recompute"
-    if rc and residual:
-        print("--op fwd+bwd_recompute covers the plain and per-head forms only", file=sys.stderr)
-        return 2
-    if rc:  # the recompute backward reads no rstd
-        bwd_row_b -= 4 * rows
-        bwd_b -= 4 * rows
-    n_fwd = {"fwd+bwd": 1, "fwd": 1, "bwd": 0, "2xfwd+bwd": 2, "fwd+bwd_recompute": 1}[op]
-    has_bwd = op != "fwd"
-    step_bytes = n_fwd * fwd_b + (bwd_b if has_bwd else 0)
-
-    def d16(bits):
-        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
-
-    w = d16(wl.w.bits) if wl.w.dtype == "bf16" else torch.from_numpy(wl.w.f32.copy()).to(dev)
-    x0 = d16(wl.xbuf if wl.xbuf is not None else wl.x)
-    dy0 = d16(wl.dy)
-    r0 = d16(wl.r) if residual else None
-    dres0 = d16(wl.dres) if with_dres else None
-
-    # buffer sets: the whole cycle spans >= 1 GiB so steps run from HBM
-    per_set = x0.numel() * 2 + dy0.numel() * 2 + 2 * rows * H * 2 * (2 if residual else 1)
-    n_sets = int(min(16, max(2, math.ceil((1 << 30) / per_set))))
-    sets = []
-    for i in range(n_sets):
-        s = dict(x=x0.clone(), dy=dy0.clone(), y=torch.empty(rows, H, dtype=torch.bfloat16, device=dev),
-                 dx=torch.empty_like(x0) if wl.xbuf is not None else torch.empty(rows, H, dtype=torch.bfloat16, device=dev),
-                 rstd=torch.empty(rows, dtype=torch.float32, device=dev),
-                 dw=torch.empty(H, dtype=torch.float32, device=dev))
-        if residual:
-            s["r"] = r0.clone()
-            s["h"] = torch.empty(rows, H, dtype=torch.bfloat16, device=dev)
-            s["dres"] = dres0.clone() if with_dres else None
-        sets.append(s)
-    del x0, dy0, r0, dres0
-
-    # separate workspaces: the deterministic partials, and the zero-filled
-    # accumulator the non-deterministic kernels keep zero-filled
-    ws_bytes_det = max(lib.rmsnorm_bwd_workspace_bytes(rows, H, wdt, 1), 256)
-    ws_bytes_nd = max(lib.rmsnorm_bwd_workspace_bytes(rows, H, wdt, 0), 256)
-    ws_det_raw = torch.empty(ws_bytes_det + 256, dtype=torch.uint8, device=dev)
-    ws_nd_raw = torch.zeros(ws_bytes_nd + 256, dtype=torch.uint8, device=dev)
-    ws_det = ws_det_raw[(-ws_det_raw.data_ptr()) % 256:]
-    ws_nd = ws_nd_raw[(-ws_nd_raw.data_ptr()) % 256:]
-    P = ctypes.c_void_p
-    ws_arg = {1: (P(ws_det.data_ptr()), ws_bytes_det), 0: (P(ws_nd.data_ptr()), ws_bytes_nd)}
-
-    if wl.xbuf is not None:
-        xv = _lib.View(T, heads, H, wl.x_stride_t, wl.x_stride_h)
-    else:
-        xv = _lib.View(T, heads, H, heads * H, H)
-    cv = _lib.View(T, heads, H, heads * H, H)
-
-    dxv = xv if wl.xbuf is not None else cv
-
-    def fwd(s, stream):
-        if residual:
-            _lib.check(lib.rmsnorm_residual_fwd(P(s["x"].data_ptr()), P(s["r"].data_ptr()),
-                                                P(w.data_ptr()), wdt, ctypes.c_float(wl.eps),
-                                                P(s["h"].data_ptr()), P(s["y"].data_ptr()),
-                                                P(s["rstd"].data_ptr()), rows, H, stream))
-        else:
-            _lib.check(lib.rmsnorm_fwd_strided(P(s["x"].data_ptr()), xv, P(w.data_ptr()), wdt,
-                                               ctypes.c_float(wl.eps), P(s["y"].data_ptr()), cv,
-                                               P(s["rstd"].data_ptr()), stream))
-
-    def bwd(s, det: int, stream):
-        wsp, ws_bytes = ws_arg[det]
-        if residual:
-            _lib.check(lib.rmsnorm_residual_bwd(P(s["dy"].data_ptr()), P(s["h"].data_ptr()),
-                                                P(s["dres"].data_ptr()) if with_dres else None,
-                                                P(s["rstd"].data_ptr()), P(w.data_ptr()), wdt, det,
-                                                P(s["dx"].data_ptr()), P(s["dw"].data_ptr()), rows, H,
-                                                wsp, ws_bytes, stream))
-        elif rc:
-            _lib.check(lib.rmsnorm_bwd_recompute(P(s["dy"].data_ptr()), cv, P(s["x"].data_ptr()), xv,
-                                                 P(w.data_ptr()), wdt, ctypes.c_float(wl.eps), det,
-                                                 P(s["dx"].data_ptr()), dxv, P(s["dw"].data_ptr()),
-                                                 wsp, ws_bytes, stream))
-        else:
-            _lib.check(lib.rmsnorm_bwd_strided(P(s["dy"].data_ptr()), cv, P(s["x"].data_ptr()), xv,
-                                               P(s["rstd"].data_ptr()), P(w.data_ptr()), wdt, det,
-                                               P(s["dx"].data_ptr()), dxv, P(s["dw"].data_ptr()),
-                                               wsp, ws_bytes, stream))
-
-    def step(s, det: int, stream):
-        for _ in range(n_fwd):
-            fwd(s, stream)
-        if has_bwd:
-            bwd(s, det, stream)
-
+def time_steps(args, torch, rn, _lib, dev, sets, fwd, step, n_fwd, has_bwd, bwd_keys,
+               step_bytes, fwd_b, bwd_row_b, bwd_b):
+    """Graph-replay and per-kernel timing of K steps (shared by both norms)."""
+    import ctypes as _ct
+    P = _ct.c_void_p
+    n_sets = len(sets)
     K, W = args.steps, args.warmup
     cur = torch.cuda.current_stream(dev)
     sp = P(cur.cuda_stream)
@@ -219,7 +97,7 @@ def main() -> int:
     for i in range(W):
         step(sets[i % n_sets], 1, sp)
     torch.cuda.synchronize()
-    out_keys = (["y"] if n_fwd else []) + (["dx", "dw"] if has_bwd else [])
+    out_keys = (["y"] if n_fwd else []) + (list(bwd_keys) if has_bwd else [])
     ref = {k: sets[0][k].clone() for k in out_keys}
 
     def capture(det: int):
@@ -312,6 +190,326 @@ def main() -> int:
         dom_name, dom_us, dom_bytes = "bwd_small", small_us, bwd_b
     achieved = dom_bytes / (dom_us * 1e-6) / 1e9
 
+    fwd_gbps = fwd_b / (fwd_us * 1e-6) / 1e9 if fwd_us else None
+    bwd_us = (bwd_row_us or 0.0) + (reduce_us or 0.0) if bwd_row_us else small_us
+    bwd_gbps = bwd_b / (bwd_us * 1e-6) / 1e9 if bwd_us else None
+
+    return dict(fwd_us=fwd_us, bwd_row_us=bwd_row_us, reduce_us=reduce_us, small_us=small_us,
+                dom_name=dom_name, dom_bytes=dom_bytes, achieved=achieved, ms_per_step=ms_per_step,
+                value=value, walls=walls, walls_nd=walls_nd, gpu_ms=gpu_ms, t_issue=t_issue, K=K,
+                W=W, median=median, fwd_gbps=fwd_gbps, bwd_gbps=bwd_gbps)
+
+
+def cpu_baseline(args, rows, step_bytes, op, oracle_rows):
+    """Time the unchanged oracle on the whole workload: called on row slices
+    from a pool of host threads, then single-threaded, each for >= --cpu-seconds."""
+    def run(threads):
+        bounds = [(rows * i // threads, rows * (i + 1) // threads) for i in range(threads)]
+        reps = 0
+        t_start = time.perf_counter()
+        with cf.ThreadPoolExecutor(max_workers=threads) as ex:
+            while True:
+                list(ex.map(lambda b: oracle_rows(*b), bounds))
+                reps += 1
+                el = time.perf_counter() - t_start
+                if el >= args.cpu_seconds:
+                    return reps, el
+
+    threads = args.cpu_threads or min(16, os.cpu_count() or 1)
+    reps_n, el_n = run(threads)
+    reps_1, el_1 = run(1)
+    model = ""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {"value": round(step_bytes * reps_n / el_n / 1e9, 4), "unit": "GB/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"the full {args.config} workload ({op}, FP64 oracle), {reps_n} repetition(s) "
+                      f"in {el_n:.1f} s, rows split over {threads} host threads of "
+                      f"{model or platform.processor()}",
+            "single_thread": {"value": round(step_bytes * reps_1 / el_1 / 1e9, 4), "cores": 1,
+                              "sample": f"{reps_1} repetition(s) in {el_1:.1f} s"}}
+
+
+def result_line(args, metric, op, value, t, step_bytes, config, traffic, cpu):
+    K = t["K"]
+    walls, walls_nd, median = t["walls"], t["walls_nd"], t["median"]
+    return {
+        "metric": metric,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": t["W"],
+        "ms_per_step": round(t["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": config,
+        "replay_ms_per_step": {"median": round(t["ms_per_step"], 5), "min": round(walls[0] / K, 5),
+                               "max": round(walls[-1] / K, 5), "replays": len(walls)},
+        "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBPS, 2),
+        "fwd_GBps": round(t["fwd_gbps"], 1) if t["fwd_gbps"] else None,
+        "bwd_GBps": round(t["bwd_gbps"], 1) if t["bwd_gbps"] else None,
+        "nondeterministic": ({"ms_per_step": round(median(walls_nd) / K, 5),
+                              "value": round(step_bytes / (median(walls_nd) / K * 1e-3) / 1e9, 2)}
+                             if walls_nd else None),
+        "kernel_us": {"fwd": t["fwd_us"], "bwd_row": t["bwd_row_us"], "dw_reduce": t["reduce_us"],
+                      "bwd_small": t["small_us"]},
+        "graph_gpu_ms": round(t["gpu_ms"], 4),
+        "eager_host_issue_ms_per_step": round(t["t_issue"] * 1e3 / K, 5),
+        "roofline": {"bound": "hbm", "kernel": t["dom_name"], "achieved": round(t["achieved"], 1),
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(t["achieved"] / HBM_PEAK_GBPS, 4),
+                     "traffic": traffic, "algorithmic_bytes": t["dom_bytes"]},
+        "cpu_baseline": cpu,
+    }
+
+
+def bench_layernorm(args, np, torch, rn, _lib, lib, synth, dev, d16) -> int:
+    P = ctypes.c_void_p
+    op = args.op
+    if op not in ("fwd+bwd", "fwd", "bwd", "2xfwd+bwd"):
+        print("--norm layernorm takes --op fwd+bwd, fwd, bwd or 2xfwd+bwd", file=sys.stderr)
+        return 2
+    if args.config is None:
+        args.config = DEFAULT_LN_CONFIG
+    wl = synth.ln_config(args.config, seed=args.seed)
+    T, H = wl.T, wl.H
+    sw = 2 if wl.gamma.dtype == "bf16" else 4
+    wdt = _lib.RMSN_BF16 if sw == 2 else _lib.RMSN_F32
+    fwd_b, bwd_row_b, bwd_b = ln_algorithmic_bytes(T, H, sw)
+    n_fwd = {"fwd+bwd": 1, "fwd": 1, "bwd": 0, "2xfwd+bwd": 2}[op]
+    has_bwd = op != "fwd"
+    step_bytes = n_fwd * fwd_b + (bwd_b if has_bwd else 0)
+
+    def wdev(wt):
+        return d16(wt.bits) if wt.dtype == "bf16" else torch.from_numpy(wt.f32.copy()).to(dev)
+
+    gam, bet = wdev(wl.gamma), wdev(wl.beta)
+    x0, dy0 = d16(wl.x), d16(wl.dy)
+    per_set = 4 * T * H * 2
+    n_sets = int(min(16, max(2, math.ceil((1 << 30) / per_set))))
+    sets = []
+    for _ in range(n_sets):
+        sets.append(dict(x=x0.clone(), dy=dy0.clone(), y=torch.empty_like(x0), dx=torch.empty_like(x0),
+                         mean=torch.empty(T, dtype=torch.float32, device=dev),
+                         rstd=torch.empty(T, dtype=torch.float32, device=dev),
+                         dg=torch.empty(H, dtype=torch.float32, device=dev),
+                         db=torch.empty(H, dtype=torch.float32, device=dev)))
+    del x0, dy0
+    ws = {}
+    for det in (0, 1):
+        nb = max(lib.layernorm_bwd_workspace_bytes(T, H, wdt, det), 256)
+        raw = torch.empty(nb + 256, dtype=torch.uint8, device=dev)
+        ws[det] = (raw, P(raw.data_ptr() + (-raw.data_ptr()) % 256), nb)
+    eps = ctypes.c_float(wl.eps)
+
+    def fwd(s, stream):
+        _lib.check(lib.layernorm_fwd(P(s["x"].data_ptr()), P(gam.data_ptr()), P(bet.data_ptr()), wdt,
+                                     eps, P(s["y"].data_ptr()), P(s["mean"].data_ptr()),
+                                     P(s["rstd"].data_ptr()), T, H, stream))
+
+    def bwd(s, det, stream):
+        _, wsp, nb = ws[det]
+        _lib.check(lib.layernorm_bwd(P(s["dy"].data_ptr()), P(s["x"].data_ptr()),
+                                     P(s["mean"].data_ptr()), P(s["rstd"].data_ptr()),
+                                     P(gam.data_ptr()), wdt, det, P(s["dx"].data_ptr()),
+                                     P(s["dg"].data_ptr()), P(s["db"].data_ptr()), T, H, wsp, nb,
+                                     stream))
+
+    def step(s, det, stream):
+        for _ in range(n_fwd):
+            fwd(s, stream)
+        if has_bwd:
+            bwd(s, det, stream)
+
+    t = time_steps(args, torch, rn, _lib, dev, sets, fwd, step, n_fwd, has_bwd, ["dx", "dg", "db"],
+                   step_bytes, fwd_b, bwd_row_b, bwd_b)
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        g64, b64 = wl.gamma.f64, wl.beta.f64
+        mu_all, rs_all, _ = oracle.ln_fwd(wl.x, g64, b64, wl.eps, want_y=False)
+
+        def oracle_rows(lo, hi):
+            mu, rs = mu_all[lo:hi], rs_all[lo:hi]
+            for _ in range(n_fwd):
+                mu, rs, _ = oracle.ln_fwd(wl.x[lo:hi], g64, b64, wl.eps)
+            if has_bwd:
+                oracle.ln_bwd(wl.dy[lo:hi], wl.x[lo:hi], mu, rs, g64)
+
+        cpu = cpu_baseline(args, T, step_bytes, op, oracle_rows)
+    config = {"workload": args.config, "norm": "layernorm", "op": op, "T": T, "H": H,
+              "w_dtype": wl.gamma.dtype, "deterministic": True, "global_batch": T, "seq_len": T,
+              "parallelism": "none (1 GPU)", "buffer_sets": n_sets}
+    out = result_line(args, f"LayerNorm {op} effective HBM GB/s, per (T,H)", op, t["value"], t,
+                      step_bytes, config, None, cpu)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--norm", choices=("rmsnorm", "layernorm"), default="rmsnorm")
+    ap.add_argument("--config", default=None)
+    ap.add_argument("--op", choices=OPS, default="fwd+bwd")
+    ap.add_argument("--replays", type=int, default=5)
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="seconds of oracle work for each of the two CPU runs")
+    ap.add_argument("--cpu-threads", type=int, default=0,
+                    help="host threads for the oracle run (0: min(16, CPUs))")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device copy of BYTES bytes 10 times (the reference "
+                         "kernel for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE) and exit")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this RMSNorm path has no multi-GPU step "
+              "(rows shard across GPUs with no exchange but one dw all-reduce, which is "
+              "not built); run with --gpus 1.", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import bwd_rmsnorm_fwd_02_amd as rn
+    from bwd_rmsnorm_fwd_02_amd import _lib
+    from tests import synth
+
+    lib = _lib.load()  # raises if the HIP library is missing: no fallback
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    if args.copy_calibration:
+        n = args.copy_calibration // 2
+        src = torch.ones(n, dtype=torch.bfloat16, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(10):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n * 2, "launches": 10}), flush=True)
+        return 0
+
+    P = ctypes.c_void_p
+    op = args.op
+
+    def d16(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    if args.norm == "layernorm":
+        return bench_layernorm(args, np, torch, rn, _lib, lib, synth, dev, d16)
+    if args.config is None:
+        args.config = DEFAULT_CONFIG
+    wl = synth.config(args.config, seed=args.seed)
+    rows, H, T, heads = wl.rows, wl.H, wl.T, wl.heads
+    residual = wl.r is not None
+    with_dres = wl.dres is not None
+    sw = 2 if wl.w.dtype == "bf16" else 4
+    wdt = _lib.RMSN_BF16 if wl.w.dtype == "bf16" else _lib.RMSN_F32
+    fwd_b, bwd_row_b, bwd_b = algorithmic_bytes(rows, H, sw, residual, with_dres)
+    rc = op == "fwd+bwd_recompute"
+    if rc and residual:
+        print("--op fwd+bwd_recompute covers the plain and per-head forms only", file=sys.stderr)
+        return 2
+    if rc:  # the recompute backward reads no rstd
+        bwd_row_b -= 4 * rows
+        bwd_b -= 4 * rows
+    n_fwd = {"fwd+bwd": 1, "fwd": 1, "bwd": 0, "2xfwd+bwd": 2, "fwd+bwd_recompute": 1}[op]
+    has_bwd = op != "fwd"
+    step_bytes = n_fwd * fwd_b + (bwd_b if has_bwd else 0)
+
+    w = d16(wl.w.bits) if wl.w.dtype == "bf16" else torch.from_numpy(wl.w.f32.copy()).to(dev)
+    x0 = d16(wl.xbuf if wl.xbuf is not None else wl.x)
+    dy0 = d16(wl.dy)
+    r0 = d16(wl.r) if residual else None
+    dres0 = d16(wl.dres) if with_dres else None
+
+    # buffer sets: the whole cycle spans >= 1 GiB so steps run from HBM
+    per_set = x0.numel() * 2 + dy0.numel() * 2 + 2 * rows * H * 2 * (2 if residual else 1)
+    n_sets = int(min(16, max(2, math.ceil((1 << 30) / per_set))))
+    sets = []
+    for i in range(n_sets):
+        s = dict(x=x0.clone(), dy=dy0.clone(), y=torch.empty(rows, H, dtype=torch.bfloat16, device=dev),
+                 dx=torch.empty_like(x0) if wl.xbuf is not None else torch.empty(rows, H, dtype=torch.bfloat16, device=dev),
+                 rstd=torch.empty(rows, dtype=torch.float32, device=dev),
+                 dw=torch.empty(H, dtype=torch.float32, device=dev))
+        if residual:
+            s["r"] = r0.clone()
+            s["h"] = torch.empty(rows, H, dtype=torch.bfloat16, device=dev)
+            s["dres"] = dres0.clone() if with_dres else None
+        sets.append(s)
+    del x0, dy0, r0, dres0
+
+    # separate workspaces: the deterministic partials, and the zero-filled
+    # accumulator the non-deterministic kernels keep zero-filled
+    ws_bytes_det = max(lib.rmsnorm_bwd_workspace_bytes(rows, H, wdt, 1), 256)
+    ws_bytes_nd = max(lib.rmsnorm_bwd_workspace_bytes(rows, H, wdt, 0), 256)
+    ws_det_raw = torch.empty(ws_bytes_det + 256, dtype=torch.uint8, device=dev)
+    ws_nd_raw = torch.zeros(ws_bytes_nd + 256, dtype=torch.uint8, device=dev)
+    ws_det = ws_det_raw[(-ws_det_raw.data_ptr()) % 256:]
+    ws_nd = ws_nd_raw[(-ws_nd_raw.data_ptr()) % 256:]
+    ws_arg = {1: (P(ws_det.data_ptr()), ws_bytes_det), 0: (P(ws_nd.data_ptr()), ws_bytes_nd)}
+
+    if wl.xbuf is not None:
+        xv = _lib.View(T, heads, H, wl.x_stride_t, wl.x_stride_h)
+    else:
+        xv = _lib.View(T, heads, H, heads * H, H)
+    cv = _lib.View(T, heads, H, heads * H, H)
+
+    dxv = xv if wl.xbuf is not None else cv
+
+    def fwd(s, stream):
+        if residual:
+            _lib.check(lib.rmsnorm_residual_fwd(P(s["x"].data_ptr()), P(s["r"].data_ptr()),
+                                                P(w.data_ptr()), wdt, ctypes.c_float(wl.eps),
+                                                P(s["h"].data_ptr()), P(s["y"].data_ptr()),
+                                                P(s["rstd"].data_ptr()), rows, H, stream))
+        else:
+            _lib.check(lib.rmsnorm_fwd_strided(P(s["x"].data_ptr()), xv, P(w.data_ptr()), wdt,
+                                               ctypes.c_float(wl.eps), P(s["y"].data_ptr()), cv,
+                                               P(s["rstd"].data_ptr()), stream))
+
+    def bwd(s, det: int, stream):
+        wsp, ws_bytes = ws_arg[det]
+        if residual:
+            _lib.check(lib.rmsnorm_residual_bwd(P(s["dy"].data_ptr()), P(s["h"].data_ptr()),
+                                                P(s["dres"].data_ptr()) if with_dres else None,
+                                                P(s["rstd"].data_ptr()), P(w.data_ptr()), wdt, det,
+                                                P(s["dx"].data_ptr()), P(s["dw"].data_ptr()), rows, H,
+                                                wsp, ws_bytes, stream))
+        elif rc:
+            _lib.check(lib.rmsnorm_bwd_recompute(P(s["dy"].data_ptr()), cv, P(s["x"].data_ptr()), xv,
+                                                 P(w.data_ptr()), wdt, ctypes.c_float(wl.eps), det,
+                                                 P(s["dx"].data_ptr()), dxv, P(s["dw"].data_ptr()),
+                                                 wsp, ws_bytes, stream))
+        else:
+            _lib.check(lib.rmsnorm_bwd_strided(P(s["dy"].data_ptr()), cv, P(s["x"].data_ptr()), xv,
+                                               P(s["rstd"].data_ptr()), P(w.data_ptr()), wdt, det,
+                                               P(s["dx"].data_ptr()), dxv, P(s["dw"].data_ptr()),
+                                               wsp, ws_bytes, stream))
+
+    def step(s, det: int, stream):
+        for _ in range(n_fwd):
+            fwd(s, stream)
+        if has_bwd:
+            bwd(s, det, stream)
+
+    t = time_steps(args, torch, rn, _lib, dev, sets, fwd, step, n_fwd, has_bwd, ["dx", "dw"],
+                   step_bytes, fwd_b, bwd_row_b, bwd_b)
+    dom_name, value = t["dom_name"], t["value"]
+
     traffic = None
     tr_path = os.path.join(ROOT, "profiles", f"traffic_{args.config}.json")
     if os.path.exists(tr_path) and op == "fwd+bwd":
@@ -319,10 +517,6 @@ def main() -> int:
         rec = json.load(open(tr_path))
         if rec.get("source_hash") == _b.source_hash() and dom_name in rec.get("kernels", {}):
             traffic = rec["kernels"][dom_name]["bytes_per_launch"]
-
-    fwd_gbps = fwd_b / (fwd_us * 1e-6) / 1e9 if fwd_us else None
-    bwd_us = (bwd_row_us or 0.0) + (reduce_us or 0.0) if bwd_row_us else small_us
-    bwd_gbps = bwd_b / (bwd_us * 1e-6) / 1e9 if bwd_us else None
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -343,71 +537,14 @@ def main() -> int:
             if has_bwd:
                 oracle.bwd(wl.dy[lo:hi], xo[lo:hi], r64, w64)
 
-        def run(threads):
-            bounds = [(rows * i // threads, rows * (i + 1) // threads) for i in range(threads)]
-            reps = 0
-            t_start = time.perf_counter()
-            with cf.ThreadPoolExecutor(max_workers=threads) as ex:
-                while True:
-                    list(ex.map(lambda b: oracle_rows(*b), bounds))
-                    reps += 1
-                    el = time.perf_counter() - t_start
-                    if el >= args.cpu_seconds:
-                        return reps, el
+        cpu = cpu_baseline(args, rows, step_bytes, op, oracle_rows)
 
-        threads = args.cpu_threads or min(16, os.cpu_count() or 1)
-        reps_n, el_n = run(threads)
-        reps_1, el_1 = run(1)
-        model = ""
-        try:
-            for line in open("/proc/cpuinfo"):
-                if line.startswith("model name"):
-                    model = line.split(":", 1)[1].strip()
-                    break
-        except OSError:
-            pass
-        cpu = {"value": round(step_bytes * reps_n / el_n / 1e9, 4), "unit": "GB/s", "cores": threads,
-               "kind": "oracle",
-               "sample": f"the full {args.config} workload ({op}, FP64 oracle), {reps_n} repetition(s) "
-                         f"in {el_n:.1f} s, rows split over {threads} host threads of "
-                         f"{model or platform.processor()}",
-               "single_thread": {"value": round(step_bytes * reps_1 / el_1 / 1e9, 4), "cores": 1,
-                                 "sample": f"{reps_1} repetition(s) in {el_1:.1f} s"}}
-
-    out = {
-        "metric": METRIC if op == "fwd+bwd" else f"RMSNorm {op} effective HBM GB/s, per (T,H)",
-        "value": round(value, 2),
-        "unit": "GB/s",
-        "n_gpus": 1,
-        "steps": K,
-        "warmup": W,
-        "ms_per_step": round(ms_per_step, 5),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic",
-        "config": {"workload": args.config, "op": op, "T": T, "heads": heads, "H": H,
-                   "w_dtype": wl.w.dtype, "residual": residual, "deterministic": True,
-                   "global_batch": rows, "seq_len": T, "parallelism": "none (1 GPU)",
-                   "buffer_sets": n_sets},
-        "replay_ms_per_step": {"median": round(ms_per_step, 5), "min": round(walls[0] / K, 5),
-                               "max": round(walls[-1] / K, 5), "replays": len(walls)},
-        "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBPS, 2),
-        "fwd_GBps": round(fwd_gbps, 1) if fwd_gbps else None,
-        "bwd_GBps": round(bwd_gbps, 1) if bwd_gbps else None,
-        "nondeterministic": ({"ms_per_step": round(median(walls_nd) / K, 5),
-                              "value": round(step_bytes / (median(walls_nd) / K * 1e-3) / 1e9, 2)}
-                             if walls_nd else None),
-        "kernel_us": {"fwd": fwd_us, "bwd_row": bwd_row_us, "dw_reduce": reduce_us,
-                      "bwd_small": small_us},
-        "graph_gpu_ms": round(gpu_ms, 4),
-        "eager_host_issue_ms_per_step": round(t_issue * 1e3 / K, 5),
-        "roofline": {"bound": "hbm", "kernel": dom_name, "achieved": round(achieved, 1),
-                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                     "traffic": traffic, "algorithmic_bytes": dom_bytes},
-        "cpu_baseline": cpu,
-    }
+    config = {"workload": args.config, "op": op, "T": T, "heads": heads, "H": H,
+              "w_dtype": wl.w.dtype, "residual": residual, "deterministic": True,
+              "global_batch": rows, "seq_len": T, "parallelism": "none (1 GPU)",
+              "buffer_sets": n_sets}
+    metric = METRIC if op == "fwd+bwd" else f"RMSNorm {op} effective HBM GB/s, per (T,H)"
+    out = result_line(args, metric, op, value, t, step_bytes, config, traffic, cpu)
     print(json.dumps(out), flush=True)
     return 0
 

@@ -229,31 +229,81 @@ def rmsnorm_residual_bwd(dy: torch.Tensor, h: torch.Tensor, rstd: torch.Tensor, 
     return dh, dw
 
 
+# ---------------------------------------------------------------- LayerNorm
+
+def layernorm_fwd(x: torch.Tensor, gamma: torch.Tensor, beta: Optional[torch.Tensor] = None,
+                  eps: float = 1e-5, y: Optional[torch.Tensor] = None,
+                  mean: Optional[torch.Tensor] = None, rstd: Optional[torch.Tensor] = None):
+    """y, mean, rstd = LayerNorm forward of contiguous x[T, H] (beta optional)."""
+    _need_bf16("x", x)
+    T, H = _contig2d("x", x)
+    if beta is not None and beta.dtype != gamma.dtype:
+        raise ValueError("gamma and beta must share one dtype")
+    y = torch.empty_like(x) if y is None else y
+    mean = torch.empty(T, dtype=torch.float32, device=x.device) if mean is None else mean
+    rstd = torch.empty(T, dtype=torch.float32, device=x.device) if rstd is None else rstd
+    _lib.check(_lib.load().layernorm_fwd(_ptr(x), _ptr(gamma), _ptr(beta), _wdtype(gamma),
+                                         float(eps), _ptr(y), _ptr(mean), _ptr(rstd), T, H,
+                                         _stream(x.device)))
+    return y, mean, rstd
+
+
+def layernorm_bwd_workspace_bytes(rows: int, H: int, w_dtype: torch.dtype,
+                                  deterministic: bool) -> int:
+    wd = _lib.RMSN_BF16 if w_dtype == torch.bfloat16 else _lib.RMSN_F32
+    return int(_lib.load().layernorm_bwd_workspace_bytes(rows, H, wd, int(bool(deterministic))))
+
+
+def layernorm_bwd(dy: torch.Tensor, x: torch.Tensor, mean: torch.Tensor, rstd: torch.Tensor,
+                  gamma: torch.Tensor, deterministic: bool = True,
+                  dx: Optional[torch.Tensor] = None, dgamma: Optional[torch.Tensor] = None,
+                  dbeta: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None):
+    """dx, dgamma, dbeta of LayerNorm for contiguous [T, H] tensors."""
+    _need_bf16("dy", dy)
+    _need_bf16("x", x)
+    T, H = _contig2d("x", x)
+    dx = torch.empty_like(x) if dx is None else dx
+    dgamma = torch.empty(H, dtype=torch.float32, device=x.device) if dgamma is None else dgamma
+    dbeta = torch.empty(H, dtype=torch.float32, device=x.device) if dbeta is None else dbeta
+    need = layernorm_bwd_workspace_bytes(T, H, gamma.dtype, deterministic)
+    ws = workspace if workspace is not None else _workspace(x.device, need)
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _lib.check(_lib.load().layernorm_bwd(_ptr(dy), _ptr(x), _ptr(mean), _ptr(rstd), _ptr(gamma),
+                                         _wdtype(gamma), int(bool(deterministic)), _ptr(dx),
+                                         _ptr(dgamma), _ptr(dbeta), T, H, _ptr(ws), nbytes,
+                                         _stream(x.device)))
+    return dx, dgamma, dbeta
+
+
 # -------------------------------------------------------------- diagnostics
 
 def rmsnorm_status_string(status: int) -> str:
     return _lib.status_string(status)
 
 
+_OPS = {"fwd": 0, "bwd": 1, "ln_fwd": 2, "ln_bwd": 3}
+
+
 def rmsnorm_route_query(op: str, rows: int, H: int, w_dtype: torch.dtype = torch.bfloat16,
                         deterministic: bool = True, residual: bool = False,
                         recompute: bool = False) -> dict:
-    """Route-table entry for op 'fwd' or 'bwd' (host only, no GPU needed);
-    the backward form is plain, residual or recompute."""
+    """Route-table entry for op 'fwd', 'bwd', 'ln_fwd' or 'ln_bwd' (host only,
+    no GPU needed); the RMSNorm backward form is plain, residual or recompute."""
     info = _lib.RouteInfo()
     wd = _lib.RMSN_BF16 if w_dtype == torch.bfloat16 else _lib.RMSN_F32
     form = 2 if recompute else (1 if residual else 0)
-    _lib.check(_lib.load().rmsnorm_route_query(0 if op == "fwd" else 1, rows, H, wd,
+    _lib.check(_lib.load().rmsnorm_route_query(_OPS[op], rows, H, wd,
                                                int(bool(deterministic)), form,
                                                ctypes.byref(info)))
     return info.as_dict()
 
 
 def rmsnorm_route_override(op: str, **knobs) -> None:
-    """Set (or, with no knobs, clear) the tuning override of op 'fwd'/'bwd'.
+    """Set (or, with no knobs, clear) the tuning override of op 'fwd', 'bwd',
+    'ln_fwd' or 'ln_bwd'.
     Knobs: vec_per_lane, unroll, rows_per_block, blocks_per_cu, partial_f64
     (1 FP64, 2 FP32), kind (RMSN_KIND_BWD_ROW_DET/_ATOMIC, non-det only)."""
-    o = 0 if op == "fwd" else 1
+    o = _OPS[op]
     if not knobs:
         _lib.check(_lib.load().rmsnorm_route_override(o, None))
         return

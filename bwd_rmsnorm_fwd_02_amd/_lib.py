@@ -40,7 +40,7 @@ EXPORTS = [
     "rmsnorm_bwd_strided", "rmsnorm_bwd_recompute", "rmsnorm_residual_bwd",
     "rmsnorm_status_string",
     "rmsnorm_route_query", "rmsnorm_route_override", "rmsnorm_timing_enable",
-    "rmsnorm_timing_read",
+    "rmsnorm_timing_read", "layernorm_fwd", "layernorm_bwd_workspace_bytes", "layernorm_bwd",
 ]
 
 
@@ -103,12 +103,16 @@ def load() -> ctypes.CDLL:
         "rmsnorm_route_override": [i32, ctypes.POINTER(RouteKnobs)],
         "rmsnorm_timing_enable": [i32],
         "rmsnorm_timing_read": [ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_double), i32],
+        "layernorm_fwd": [p, p, p, i32, f32, p, p, p, i64, i64, p],
+        "layernorm_bwd_workspace_bytes": [i64, i64, i32, i32],
+        "layernorm_bwd": [p, p, p, p, p, i32, i32, p, p, p, i64, i64, p, sz, p],
     }
     for name, args in sig.items():
         f = getattr(lib, name)
         f.argtypes = args
         f.restype = ctypes.c_int
     lib.rmsnorm_bwd_workspace_bytes.restype = ctypes.c_size_t
+    lib.layernorm_bwd_workspace_bytes.restype = ctypes.c_size_t
     lib.rmsnorm_status_string.restype = ctypes.c_char_p
     _lib = lib
     return lib

@@ -320,6 +320,119 @@ int bwd_impl(const void* dy, const rmsn_view_t& dyv, const void* x, const rmsn_v
     return st;
 }
 
+// --------------------------------------------------------------- LayerNorm
+
+int ln_fwd_impl(const void* x, const void* gamma, const void* beta, rmsn_dtype_t wdt, float eps,
+                void* y, float* mean, float* rstd, int64_t T, int64_t H, hipStream_t s) {
+    int st;
+    if ((st = check_dtype(wdt)) != RMSN_OK) return st;
+    const rmsn_view_t v = contiguous(T, H);
+    if ((st = check_shape(v)) != RMSN_OK) return st;
+    if ((st = check_eps(eps)) != RMSN_OK) return st;
+    if (T == 0) return RMSN_OK;
+    if (!x || !gamma || !y || !mean || !rstd) return RMSN_ERR_NULL;
+    int64_t ex, ey;
+    if ((st = check_layout(x, v, &ex)) != RMSN_OK) return st;
+    if ((st = check_layout(y, v, &ey)) != RMSN_OK) return st;
+    if (!aligned(gamma, 16) || (beta && !aligned(beta, 16)) || !aligned(mean, 4) || !aligned(rstd, 4))
+        return RMSN_ERR_ALIGN;
+    const Span sx = span_of(x, ex, 2), sy = span_of(y, ey, 2);
+    const Span sg = span_of(gamma, H, wsize(wdt));
+    const Span sb = beta ? span_of(beta, H, wsize(wdt)) : Span{0, 0};
+    const Span sm = span_of(mean, T, 4), sr = span_of(rstd, T, 4);
+    if (!(x == y) && overlap(sy, sx)) return RMSN_ERR_ALIAS;  // y may overwrite x exactly
+    if (overlap(sy, sg) || overlap(sy, sb) || overlap(sy, sm) || overlap(sy, sr)) return RMSN_ERR_ALIAS;
+    for (const Span& o : {sm, sr})
+        if (overlap(o, sx) || overlap(o, sg) || overlap(o, sb)) return RMSN_ERR_ALIAS;
+    if (overlap(sm, sr)) return RMSN_ERR_ALIAS;
+
+    Route rt;
+    if ((st = route(2, T, H, wdt, 1, kFormPlain, &rt)) != RMSN_OK) return st;
+    LnFwdParams p;
+    memset(&p, 0, sizeof p);
+    p.x = static_cast<const uint16_t*>(x);
+    p.y = static_cast<uint16_t*>(y);
+    p.mean = mean;
+    p.rstd = rstd;
+    p.gamma = gamma;
+    p.beta = beta;
+    p.rows = T;
+    p.H = (int32_t)H;
+    p.nvec = (int32_t)(H / kVec);
+    p.tpr = rt.r.lanes_per_row;
+    p.rpb = rt.r.rows_per_block;
+    p.eps = eps;
+    timer_begin(RMSN_TIMER_FWD, s);
+    st = launch_ln_fwd(p, rt, wdt, s);
+    timer_end(RMSN_TIMER_FWD, s);
+    return st;
+}
+
+int ln_bwd_impl(const void* dy, const void* x, const float* mean, const float* rstd,
+                const void* gamma, rmsn_dtype_t wdt, int det, void* dx, float* dgamma,
+                float* dbeta, int64_t T, int64_t H, void* ws, size_t ws_bytes, hipStream_t s) {
+    int st;
+    if ((st = check_dtype(wdt)) != RMSN_OK) return st;
+    const rmsn_view_t v = contiguous(T, H);
+    if ((st = check_shape(v)) != RMSN_OK) return st;
+    if (!dgamma || !dbeta) return RMSN_ERR_NULL;
+    if (!aligned(dgamma, 4) || !aligned(dbeta, 4)) return RMSN_ERR_ALIGN;
+    const Span sdg = span_of(dgamma, H, 4), sdb = span_of(dbeta, H, 4);
+    if (overlap(sdg, sdb)) return RMSN_ERR_ALIAS;
+    if (T == 0) {
+        // column sums over zero rows are zero
+        timer_begin(RMSN_TIMER_INIT, s);
+        st = launch_fill_zero(dgamma, (size_t)H * 4, s);
+        if (st == RMSN_OK) st = launch_fill_zero(dbeta, (size_t)H * 4, s);
+        timer_end(RMSN_TIMER_INIT, s);
+        return st;
+    }
+    if (!dy || !x || !mean || !rstd || !gamma || !dx) return RMSN_ERR_NULL;
+    int64_t ex, edy, edx;
+    if ((st = check_layout(x, v, &ex)) != RMSN_OK) return st;
+    if ((st = check_layout(dy, v, &edy)) != RMSN_OK) return st;
+    if ((st = check_layout(dx, v, &edx)) != RMSN_OK) return st;
+    if (!aligned(gamma, 16) || !aligned(mean, 4) || !aligned(rstd, 4)) return RMSN_ERR_ALIGN;
+    const Span sx = span_of(x, ex, 2), sdy = span_of(dy, edy, 2), sdx = span_of(dx, edx, 2);
+    const Span sg = span_of(gamma, H, wsize(wdt));
+    const Span sm = span_of(mean, T, 4), sr = span_of(rstd, T, 4);
+    for (const Span& o : {sdx, sdg, sdb}) {
+        if (overlap(o, sx) || overlap(o, sdy) || overlap(o, sg) || overlap(o, sm) || overlap(o, sr))
+            return RMSN_ERR_ALIAS;
+    }
+    if (overlap(sdx, sdg) || overlap(sdx, sdb)) return RMSN_ERR_ALIAS;
+
+    Route rt;
+    if ((st = route(3, T, H, wdt, det, kFormPlain, &rt)) != RMSN_OK) return st;
+    if (!ws || !aligned(ws, 256) || ws_bytes < rt.workspace) return RMSN_ERR_WORKSPACE;
+    const Span sws = span_of(ws, (int64_t)rt.workspace, 1);
+    for (const Span& o : {sx, sdy, sdx, sg, sm, sr, sdg, sdb})
+        if (overlap(sws, o)) return RMSN_ERR_ALIAS;
+
+    LnBwdParams p;
+    memset(&p, 0, sizeof p);
+    p.dy = static_cast<const uint16_t*>(dy);
+    p.x = static_cast<const uint16_t*>(x);
+    p.mean = mean;
+    p.rstd = rstd;
+    p.gamma = gamma;
+    p.dx = static_cast<uint16_t*>(dx);
+    p.partial = ws;
+    p.rows = T;
+    p.H = (int32_t)H;
+    p.nvec = (int32_t)(H / kVec);
+    p.tpr = rt.r.lanes_per_row;
+    p.rpb = rt.r.rows_per_block;
+    timer_begin(RMSN_TIMER_BWD_ROW, s);
+    st = launch_ln_bwd_row(p, rt, wdt, s);
+    timer_end(RMSN_TIMER_BWD_ROW, s);
+    if (st != RMSN_OK) return st;
+    timer_begin(RMSN_TIMER_DW_REDUCE, s);
+    st = launch_col_reduce(ws, rt, (int32_t)(2 * H), dgamma, dbeta, (int32_t)H, s);
+    timer_end(RMSN_TIMER_DW_REDUCE, s);
+    return st;
+}
+
 }  // namespace
 
 // ==================================================================== C ABI
@@ -399,6 +512,27 @@ int rmsnorm_residual_bwd(const void* dy, const void* h, const void* dres, const 
                     dw, workspace, workspace_bytes, kFormResidual, 0.f, stream);
 }
 
+int layernorm_fwd(const void* x, const void* gamma, const void* beta, rmsn_dtype_t w_dtype,
+                  float eps, void* y, float* mean, float* rstd, int64_t T, int64_t H,
+                  hipStream_t stream) {
+    return ln_fwd_impl(x, gamma, beta, w_dtype, eps, y, mean, rstd, T, H, stream);
+}
+
+size_t layernorm_bwd_workspace_bytes(int64_t rows, int64_t H, rmsn_dtype_t w_dtype,
+                                     int deterministic) {
+    Route rt;
+    if (route(3, rows, H, w_dtype, deterministic, kFormPlain, &rt) != RMSN_OK) return 0;
+    return rt.workspace;
+}
+
+int layernorm_bwd(const void* dy, const void* x, const float* mean, const float* rstd,
+                  const void* gamma, rmsn_dtype_t w_dtype, int deterministic, void* dx,
+                  float* dgamma, float* dbeta, int64_t T, int64_t H, void* workspace,
+                  size_t workspace_bytes, hipStream_t stream) {
+    return ln_bwd_impl(dy, x, mean, rstd, gamma, w_dtype, deterministic, dx, dgamma, dbeta, T, H,
+                       workspace, workspace_bytes, stream);
+}
+
 const char* rmsnorm_status_string(int status) {
     switch (status) {
         case RMSN_OK: return "ok";
@@ -427,7 +561,7 @@ int rmsnorm_route_query(int op, int64_t rows, int64_t H, rmsn_dtype_t w_dtype, i
                         int form, rmsn_route_t* out) {
     if (!out) return RMSN_ERR_NULL;
     Route rt;
-    const int st = route(op, rows, H, w_dtype, deterministic, op == 0 ? kFormPlain : form, &rt);
+    const int st = route(op, rows, H, w_dtype, deterministic, op == 1 ? form : kFormPlain, &rt);
     *out = rt.r;
     return st;
 }

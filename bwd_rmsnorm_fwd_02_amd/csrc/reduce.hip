@@ -3,16 +3,19 @@
 
 namespace rmsn {
 
-// Fixed-order reduction of P partial rows. A block owns 128 contiguous
-// bytes of columns (8 chunks of 16 bytes, so every partial row is read with
-// whole cache lines) and S = blockDim/8 slices: thread (chunk c, slice s)
-// sums partial rows s, s + S, s + 2S, ... in increasing order, four loads in
-// flight at a time. The slice sums are then added in a fixed order: a
-// butterfly over the 8 slices each wave holds, then the waves in index
+// Fixed-order reduction of P partial rows of W columns. A block owns 128
+// contiguous bytes of columns (8 chunks of 16 bytes, so every partial row is
+// read with whole cache lines) and S = blockDim/8 slices: thread (chunk c,
+// slice s) sums partial rows s, s + S, s + 2S, ... in increasing order, four
+// loads in flight at a time. The slice sums are then added in a fixed order:
+// a butterfly over the 8 slices each wave holds, then the waves in index
 // order. Nothing depends on timing, so the result is bit-reproducible.
+// Columns below `split` go to out0, the others to out1 (LayerNorm's dgamma
+// and dbeta share one partial row); split is a multiple of the chunk width.
 template <typename PT>
 __global__ void __launch_bounds__(1024) k_dw_reduce(const PT* __restrict__ part, int64_t P,
-                                                    int32_t H, float* __restrict__ dw) {
+                                                    int32_t H, float* __restrict__ dw,
+                                                    float* __restrict__ out1, int32_t split) {
     constexpr int CPC = 16 / sizeof(PT);  // columns per 16-byte chunk
     constexpr int CC = 8;                 // chunks per block
     __shared__ double sm_red[16][CC * CPC];
@@ -69,11 +72,12 @@ __global__ void __launch_bounds__(1024) k_dw_reduce(const PT* __restrict__ part,
     }
     __syncthreads();
     if (threadIdx.x < CC && col_ok) {
+        float* dst = col0 < split ? dw + col0 : out1 + (col0 - split);
 #pragma unroll
         for (int e = 0; e < CPC; ++e) {
             double t = 0.0;
             for (int w = 0; w < nwaves; ++w) t += sm_red[w][cc * CPC + e];
-            dw[col0 + e] = (float)t;
+            dst[e] = (float)t;
         }
     }
 }
@@ -88,17 +92,22 @@ __global__ void __launch_bounds__(256) k_fill_zero(uint4* p, int64_t n16, uint8_
     if (i0 < ntail) tail[i0] = 0;
 }
 
-int launch_dw_reduce(const BwdParams& p, const Route& rt, hipStream_t s) {
+int launch_col_reduce(const void* partial, const Route& rt, int32_t W, float* out0, float* out1,
+                      int32_t split, hipStream_t s) {
     const unsigned threads = (unsigned)rt.r.reduce_threads;
     dim3 grid((unsigned)rt.r.reduce_grid), block(threads);
     const size_t lds = 0;
     if (rt.r.partial_f64)
-        launch_kernel(k_dw_reduce<double>, grid, block, lds, s,
-                           static_cast<const double*>(p.partial), (int64_t)rt.r.partials, p.H, p.dw);
+        launch_kernel(k_dw_reduce<double>, grid, block, lds, s, static_cast<const double*>(partial),
+                      (int64_t)rt.r.partials, W, out0, out1, split);
     else
-        launch_kernel(k_dw_reduce<float>, grid, block, lds, s,
-                           static_cast<const float*>(p.partial), (int64_t)rt.r.partials, p.H, p.dw);
+        launch_kernel(k_dw_reduce<float>, grid, block, lds, s, static_cast<const float*>(partial),
+                      (int64_t)rt.r.partials, W, out0, out1, split);
     return hipGetLastError() == hipSuccess ? RMSN_OK : RMSN_ERR_LAUNCH;
+}
+
+int launch_dw_reduce(const BwdParams& p, const Route& rt, hipStream_t s) {
+    return launch_col_reduce(p.partial, rt, p.H, p.dw, nullptr, p.H, s);
 }
 
 int launch_fill_zero(void* ptr, size_t bytes, hipStream_t s) {
@@ -128,6 +137,14 @@ int launch_bwd_small(const BwdParams& p, const Route& rt, rmsn_dtype_t wdt, bool
                      hipStream_t s) {
     return wdt == RMSN_BF16 ? launch_bwd_small_bf16w(p, rt, residual, s)
                             : launch_bwd_small_f32w(p, rt, residual, s);
+}
+
+int launch_ln_fwd(const LnFwdParams& p, const Route& rt, rmsn_dtype_t wdt, hipStream_t s) {
+    return wdt == RMSN_BF16 ? launch_ln_fwd_bf16w(p, rt, s) : launch_ln_fwd_f32w(p, rt, s);
+}
+
+int launch_ln_bwd_row(const LnBwdParams& p, const Route& rt, rmsn_dtype_t wdt, hipStream_t s) {
+    return wdt == RMSN_BF16 ? launch_ln_bwd_row_bf16w(p, rt, s) : launch_ln_bwd_row_f32w(p, rt, s);
 }
 
 }  // namespace rmsn

@@ -95,6 +95,15 @@ __device__ __forceinline__ void use_now(const uint4& v) {
 }
 __device__ __forceinline__ void use_now(float v) { asm volatile("" ::"v"(v)); }
 
+// A copy of v that the compiler cannot see through: values derived from it
+// are recomputed rather than kept live from an earlier identical expression.
+// Used where the unpacked row would otherwise stay in registers across a row
+// reduction (twice the registers of the packed 16-byte vectors).
+__device__ __forceinline__ uint4 opaque(uint4 v) {
+    asm volatile("" : "+v"(v.x), "+v"(v.y), "+v"(v.z), "+v"(v.w));
+    return v;
+}
+
 // Workgroup barrier that orders LDS traffic only. A plain __syncthreads()
 // also waits for the wave's outstanding global loads and stores (the vector
 // memory counter covers both on gfx9-family parts), which would drain the

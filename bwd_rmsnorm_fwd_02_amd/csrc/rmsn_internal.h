@@ -68,12 +68,44 @@ struct BwdParams {
     float eps;              // recompute form only
 };
 
+// LayerNorm (contiguous [rows, H]).
+struct LnFwdParams {
+    const uint16_t* x;
+    uint16_t* y;
+    float* mean;
+    float* rstd;
+    const void* gamma;
+    const void* beta;       // may be null: zero bias
+    int64_t rows;
+    int32_t H;
+    int32_t nvec;
+    int32_t tpr;
+    int32_t rpb;
+    float eps;
+};
+
+struct LnBwdParams {
+    const uint16_t* dy;
+    const uint16_t* x;
+    const float* mean;
+    const float* rstd;
+    const void* gamma;
+    uint16_t* dx;
+    void* partial;          // [P, 2H] FP32 or FP64: dgamma sums, then dbeta sums
+    int64_t rows;
+    int32_t H;
+    int32_t nvec;
+    int32_t tpr;
+    int32_t rpb;
+};
+
 struct Route {
     rmsn_route_t r;
     size_t workspace;       // bytes needed
 };
 
-// Route table (route.cpp). op 0 fwd, 1 bwd; form kForm* (backward).
+// Route table (route.cpp). op 0 fwd, 1 bwd, 2 LayerNorm fwd, 3 LayerNorm
+// bwd; form kForm* (RMSNorm backward).
 int route(int op, int64_t rows, int64_t H, rmsn_dtype_t wdt, int det, int form, Route* out);
 // Tuning override of the route table (NULL clears).
 int set_route_knobs(int op, const rmsn_route_knobs_t* knobs);
@@ -85,6 +117,16 @@ int launch_fwd(const FwdParams& p, const Route& rt, rmsn_dtype_t wdt, bool resid
 int launch_bwd_row(const BwdParams& p, const Route& rt, rmsn_dtype_t wdt, int form,
                    hipStream_t s);
 int launch_dw_reduce(const BwdParams& p, const Route& rt, hipStream_t s);
+// Column reduce of rt.partials partial rows of W columns: columns < split go
+// to out0, the rest to out1.
+int launch_col_reduce(const void* partial, const Route& rt, int32_t W, float* out0, float* out1,
+                      int32_t split, hipStream_t s);
+int launch_ln_fwd(const LnFwdParams& p, const Route& rt, rmsn_dtype_t wdt, hipStream_t s);
+int launch_ln_bwd_row(const LnBwdParams& p, const Route& rt, rmsn_dtype_t wdt, hipStream_t s);
+int launch_ln_fwd_bf16w(const LnFwdParams& p, const Route& rt, hipStream_t s);
+int launch_ln_fwd_f32w(const LnFwdParams& p, const Route& rt, hipStream_t s);
+int launch_ln_bwd_row_bf16w(const LnBwdParams& p, const Route& rt, hipStream_t s);
+int launch_ln_bwd_row_f32w(const LnBwdParams& p, const Route& rt, hipStream_t s);
 int launch_bwd_small(const BwdParams& p, const Route& rt, rmsn_dtype_t wdt, bool residual,
                      hipStream_t s);
 int launch_fill_zero(void* ptr, size_t bytes, hipStream_t s);

@@ -26,8 +26,14 @@ constexpr int64_t kSmallRows = 64;
 // (the FP32 rounding of each partial adds ~3e-8 * sqrt(T) absolute error).
 constexpr int64_t kPartialF32MaxRows = 8192;
 
-bool g_have_knobs[2] = {false, false};
-rmsn_route_knobs_t g_knobs[2];
+// LayerNorm's backward keeps twice the FP64 accumulators (dgamma and
+// dbeta): one vector per lane where the RMSNorm table takes two for wide rows.
+constexpr int kOps = 4;
+bool g_have_knobs[kOps] = {false, false, false, false};
+rmsn_route_knobs_t g_knobs[kOps];
+// Largest dynamic LDS a block asks for (the LayerNorm slot combine holds 2H
+// doubles when a block has several row groups).
+constexpr size_t kMaxLds = 64 * 1024;
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -100,8 +106,33 @@ Shape lookup(const Entry (&t)[N], int nvec) {
     return Shape{1, 1, 0, 0};
 }
 
+// LayerNorm, timed in step mode at the shapes of the TE page's
+// normalization table (8192 tokens x 3584, 4096, 8192, 16384) and at
+// 65536 x 2048. Its forward holds no FP64 accumulators and does two row
+// exchanges, so it takes four vectors per lane and fewer lanes per row.
+constexpr Entry kLnFwdTable[] = {
+    {32, 4, 1, 256, 2},     // H <= 256
+    {64, 4, 1, 256, 2},     // H <= 512
+    {256, 4, 1, 256, 2},    // H <= 2048
+    {512, 4, 1, 256, 2},    // H <= 4096: 128 lanes per row, 2 rows per block
+    {1024, 4, 1, 256, 2},   // H <= 8192: 256 lanes, one row per block, 2 blocks per CU
+    {1 << 30, 4, 1, 0, 1},  // H <= 16384
+};
+constexpr Entry kLnBwdTable[] = {
+    {32, 2, 1, 128, 4},     // H <= 256
+    {64, 2, 1, 128, 4},     // H <= 512
+    {192, 1, 1, 768, 1},    // H <= 1536
+    {256, 2, 2, 256, 2},    // H <= 2048: 128 lanes, 2 rows per iteration, 2 blocks per CU
+    {512, 1, 1, 0, 2},      // H <= 4096
+    {640, 1, 1, 0, 1},      // H <= 5120
+    {1024, 1, 1, 0, 1},     // H <= 8192: 1024 lanes, one row per block
+    {1 << 30, 4, 1, 0, 1},  // H <= 16384: 512 lanes, four vectors each
+};
+
 Shape default_fwd(int nvec) { return lookup(kFwdTable, nvec); }
 Shape default_bwd(int nvec) { return lookup(kBwdTable, nvec); }
+Shape default_ln_fwd(int nvec) { return lookup(kLnFwdTable, nvec); }
+Shape default_ln_bwd(int nvec) { return lookup(kLnBwdTable, nvec); }
 
 // Fill the row-kernel part of a route from a shape; 0 fields take defaults.
 // The checks mirror what the kernels are compiled for: (NV, U) pairs with
@@ -109,7 +140,10 @@ Shape default_bwd(int nvec) { return lookup(kBwdTable, nvec); }
 // fits in one wave, <= 512 when NV * U >= 4, else <= 1024.
 int row_shape(int op, int nvec, Shape sh, rmsn_route_t& r) {
     const int nv = sh.nv;
-    if (!(nv == 1 || nv == 2 || (nv == 4 && op == 0))) return RMSN_ERR_SHAPE;
+    // NV 4: the forwards (ops 0, 2), and the LayerNorm backward (op 3) with U = 1
+    const bool nv_ok = nv == 1 || nv == 2 || (nv == 4 && (op == 0 || op == 2)) ||
+                       (nv == 4 && op == 3 && sh.unroll == 1);
+    if (!nv_ok) return RMSN_ERR_SHAPE;
     const int tpr = lanes_per_row(nvec, nv);
     if (tpr > 1024) return RMSN_ERR_SHAPE;
     const int u = sh.unroll;
@@ -146,7 +180,7 @@ void apply_knobs(const rmsn_route_knobs_t& k, Shape& sh) {
 }  // namespace
 
 int set_route_knobs(int op, const rmsn_route_knobs_t* k) {
-    if (op != 0 && op != 1) return RMSN_ERR_SHAPE;
+    if (op < 0 || op >= kOps) return RMSN_ERR_SHAPE;
     if (!k) {
         g_have_knobs[op] = false;
         return RMSN_OK;
@@ -168,11 +202,52 @@ int route(int op, int64_t rows, int64_t H, rmsn_dtype_t wdt, int det, int form, 
     if (wdt != RMSN_BF16 && wdt != RMSN_F32) return RMSN_ERR_DTYPE;
     if (H < kVec || H > kMaxH || H % kVec != 0 || rows < 0 || rows > INT32_MAX)
         return RMSN_ERR_SHAPE;
-    if (op != 0 && op != 1) return RMSN_ERR_SHAPE;
+    if (op < 0 || op >= kOps) return RMSN_ERR_SHAPE;
     if (form != kFormPlain && form != kFormResidual && form != kFormRecompute) return RMSN_ERR_SHAPE;
     const int nvec = (int)(H / kVec);
     rmsn_route_t& r = out->r;
     int st;
+
+    if (op == 2) {  // LayerNorm forward
+        Shape sh = default_ln_fwd(nvec);
+        if (g_have_knobs[2]) apply_knobs(g_knobs[2], sh);
+        if ((st = row_shape(0, nvec, sh, r)) != RMSN_OK) return st;
+        const int nv = r.vec_per_lane, u = r.unroll;  // compiled pairs
+        if (!((nv == 1 && u <= 2) || (nv == 2 && u <= 4 && u != 3) || (nv == 4 && u == 1)))
+            return RMSN_ERR_SHAPE;
+        r.kind = RMSN_KIND_FWD_ROW;
+        const int bpc = sh.bpc > 0 ? sh.bpc : (2048 / r.block_threads > 0 ? 2048 / r.block_threads : 1);
+        const int64_t cap = (int64_t)kPartitionCUs * bpc;
+        const int64_t g = ceil_div(rows, (int64_t)r.rows_per_block * r.unroll);
+        r.grid = g < cap ? g : cap;
+        if (r.grid < 1) r.grid = 1;
+        return RMSN_OK;
+    }
+
+    if (op == 3) {  // LayerNorm backward: row kernel + [P, 2H] partials at every T
+        Shape sh = default_ln_bwd(nvec);
+        const rmsn_route_knobs_t* k = g_have_knobs[3] ? &g_knobs[3] : nullptr;
+        if (k) apply_knobs(*k, sh);
+        if ((st = row_shape(3, nvec, sh, r)) != RMSN_OK) return st;
+        if (r.unroll > 2) return RMSN_ERR_SHAPE;  // compiled pairs
+        if (r.rows_per_block > 1 && (size_t)16 * H > kMaxLds) return RMSN_ERR_SHAPE;
+        int bpc = sh.bpc > 0 ? sh.bpc : 1024 / r.block_threads;
+        if (bpc < 1) bpc = 1;
+        const int64_t cap = (int64_t)kPartitionCUs * bpc;
+        const int64_t g = ceil_div(rows, 4LL * r.rows_per_block * r.unroll);
+        r.grid = g < cap ? g : cap;
+        if (r.grid < 1) r.grid = 1;
+        r.kind = RMSN_KIND_BWD_ROW_DET;
+        r.partial_f64 = rows > kPartialF32MaxRows ? 1 : 0;
+        if (k && k->partial_f64) r.partial_f64 = k->partial_f64 == 1 ? 1 : 0;
+        r.partials = r.grid;
+        const int psize = r.partial_f64 ? 8 : 4;
+        r.reduce_grid = ceil_div(2 * H * psize, 128);
+        r.reduce_threads = 1024;
+        out->workspace = align256((size_t)r.partials * (size_t)(2 * H) * psize);
+        (void)det;
+        return RMSN_OK;
+    }
 
     if (op == 0) {
         Shape sh = default_fwd(nvec);
@@ -215,6 +290,7 @@ int route(int op, int64_t rows, int64_t H, rmsn_dtype_t wdt, int det, int form, 
     const rmsn_route_knobs_t* k = g_have_knobs[1] ? &g_knobs[1] : nullptr;
     if (k) apply_knobs(*k, sh);
     if ((st = row_shape(1, nvec, sh, r)) != RMSN_OK) return st;
+    if (r.rows_per_block > 1 && (size_t)8 * H > kMaxLds) return RMSN_ERR_SHAPE;
     // Every block should be resident at once (the partition is fixed, so a
     // second round of blocks would lengthen the tail): by default 16 waves
     // per CU.

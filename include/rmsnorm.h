@@ -161,6 +161,41 @@ int rmsnorm_residual_bwd(const void* dy, const void* h, const void* dres,
                          int deterministic, void* dh, float* dw, int64_t T, int64_t H,
                          void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* -------------------------------------------------------------- LayerNorm
+ *
+ * The adjacent normalisation of the same training stacks (ROCm
+ * TransformerEngine PR "Microbenchmarking and CI performance regression
+ * test", benchmark_normalization table: RMSNorm and LayerNorm forward and
+ * backward, BF16, on MI355). Contiguous x[T, H] BF16; gamma and beta [H] BF16
+ * or FP32 (the same dtype):
+ *   forward   mean_t = (1/H) sum_j x_tj, var_t = (1/H) sum_j (x_tj - mean_t)^2,
+ *             rstd_t = 1/sqrt(var_t + eps),
+ *             y_tj = BF16((x_tj - mean_t) * rstd_t * gamma_j + beta_j)
+ *   backward  xhat = (x - mean) * rstd, g = dy * gamma,
+ *             dx = BF16(rstd * (g - mean_j(g) - xhat * mean_j(g * xhat))),
+ *             dgamma_j = sum_t dy_tj * xhat_tj,  dbeta_j = sum_t dy_tj
+ * Conventions, modes and errors as for RMSNorm above (deterministic != 0:
+ * dgamma and dbeta bit-identical run to run and across devices).
+ */
+
+/* Forward: y [T, H] BF16 (may be x itself, exactly), mean and rstd [T]
+ * FP32. beta may be NULL (no bias). */
+int layernorm_fwd(const void* x, const void* gamma, const void* beta, rmsn_dtype_t w_dtype,
+                  float eps, void* y, float* mean, float* rstd, int64_t T, int64_t H,
+                  hipStream_t stream);
+
+/* Workspace bytes layernorm_bwd needs (its [P, 2H] partial sums). */
+size_t layernorm_bwd_workspace_bytes(int64_t rows, int64_t H, rmsn_dtype_t w_dtype,
+                                     int deterministic);
+
+/* Backward at the forward's mean and rstd: dx [T, H] BF16, dgamma and dbeta
+ * [H] FP32 (overwritten; zero when T == 0). The workspace is scratch, as
+ * for rmsnorm_bwd. */
+int layernorm_bwd(const void* dy, const void* x, const float* mean, const float* rstd,
+                  const void* gamma, rmsn_dtype_t w_dtype, int deterministic, void* dx,
+                  float* dgamma, float* dbeta, int64_t T, int64_t H, void* workspace,
+                  size_t workspace_bytes, hipStream_t stream);
+
 /* ------------------------------------------------------------ diagnostics */
 
 /* Static description of an error code (never NULL). */
@@ -189,9 +224,10 @@ typedef struct {
 } rmsn_route_t;
 
 /* The route table: which kernel and launch shape serve this problem.
- * op: 0 forward, 1 backward. form (backward only; ignored for the forward):
- * 0 plain (rmsnorm_bwd, rmsnorm_bwd_strided), 1 residual
- * (rmsnorm_residual_bwd), 2 recompute (rmsnorm_bwd_recompute).
+ * op: 0 forward, 1 backward, 2 LayerNorm forward, 3 LayerNorm backward.
+ * form (op 1 only; ignored otherwise): 0 plain (rmsnorm_bwd,
+ * rmsnorm_bwd_strided), 1 residual (rmsnorm_residual_bwd), 2 recompute
+ * (rmsnorm_bwd_recompute).
  * Pure host function; needs no GPU.
  * Returns RMSN_OK or RMSN_ERR_SHAPE / RMSN_ERR_DTYPE / RMSN_ERR_NULL. */
 int rmsnorm_route_query(int op, int64_t rows, int64_t H, rmsn_dtype_t w_dtype,
@@ -203,7 +239,8 @@ int rmsnorm_route_query(int op, int64_t rows, int64_t H, rmsn_dtype_t w_dtype,
  * the next call of that op fail with RMSN_ERR_SHAPE instead of launching.
  * Overriding the backward changes the deterministic partition, hence the dw
  * bits (they stay reproducible for a fixed setting). The small-T column-task
- * route is not affected. Process-wide; NULL clears. */
+ * route is not affected. op as for rmsnorm_route_query. Process-wide; NULL
+ * clears. */
 typedef struct {
     int vec_per_lane;   /* 1, 2 or 4 (backward: 1 or 2) */
     int unroll;         /* 1, 2 or 4; only 1 when a row spans several waves */

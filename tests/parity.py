@@ -106,3 +106,46 @@ def oracle_rstd32(x_bits: np.ndarray, w64: np.ndarray, eps: float):
     """The oracle's rstd in FP64 and rounded to FP32 (the backward's input)."""
     r64, _ = oracle.fwd(x_bits, w64, eps, want_y=False)
     return r64, oracle.round_f32(r64)
+
+
+# ------------------------------------------------------------------ LayerNorm
+#
+# The same budgets for LayerNorm (the adjacent normalisation of ROCm
+# TransformerEngine PR "Microbenchmarking and CI performance regression
+# test", benchmark_normalization): dgamma and dbeta per element as dw; y and
+# dx within one BF16 ulp of the FP64 value rounded to BF16, with the same
+# cancellation exemption (y = xhat*gamma + beta can cancel too, so y gets a
+# bound as well); mean and rstd within relative 1e-6 (the mean relative to
+# the row's scale sqrt(mean^2 + var), since it can be near zero).
+
+def ln_y_bound(x64, mu64, rstd64, gamma64, beta64):
+    """FP32 evaluation bound for y = (x - mean)*rstd*gamma + beta, from a
+    forward whose mean and rstd carry their own FP32 rounding."""
+    xhat = (x64 - mu64[:, None]) * rstd64[:, None]
+    scale = rstd64[:, None] * (np.abs(x64) + np.abs(mu64)[:, None])
+    b = 0.0 if beta64 is None else np.abs(beta64)[None, :]
+    return U32 * (4 * scale * np.abs(gamma64)[None, :] + 4 * np.abs(xhat * gamma64[None, :]) + 2 * b)
+
+
+def ln_dx_bound(x64, dy64, gamma64, mu, rstd, c, H):
+    """FP32 evaluation bound for dx = rstd*(g - c1 - xhat*c2) at the given
+    (FP32) mean and rstd; c = [c1, c2] per row."""
+    g = np.abs(dy64 * gamma64[None, :])
+    xh = np.abs((x64 - mu[:, None]) * rstd[:, None])
+    c1 = np.abs(c[:, 0])[:, None]
+    c2 = np.abs(c[:, 1])[:, None]
+    mg = np.mean(g, axis=1)[:, None]
+    mgx = np.mean(g * xh, axis=1)[:, None]
+    gamma_c = (math.log2(max(H, 2)) + 16.0) * U32
+    return rstd[:, None] * (4 * U32 * (g + c1 + xh * c2) + 2 * U32 * xh * c2
+                            + gamma_c * (mg + xh * mgx))
+
+
+def check_ln_stats(name: str, mean_gpu, rstd_gpu, mu64, rstd64, var64) -> None:
+    mean_gpu = np.asarray(mean_gpu, np.float64)
+    scale = np.sqrt(mu64 * mu64 + var64)
+    bad = np.abs(mean_gpu - mu64) > RSTD_RTOL * scale
+    if np.any(bad):
+        i = int(np.argmax(bad))
+        raise AssertionError(f"{name}: mean off at row {i}: {mean_gpu[i]!r} vs {mu64[i]!r}")
+    check_rstd(name + " rstd", rstd_gpu, rstd64)

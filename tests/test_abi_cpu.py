@@ -26,7 +26,8 @@ P = ctypes.c_void_p
 def _declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][\w\s\*]*?\b(rmsnorm_\w+)\s*\(", text, flags=re.M)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][\w\s\*]*?\b((?:rmsnorm|layernorm)_\w+)\s*\(",
+                       text, flags=re.M)
     return sorted(set(names))
 
 
@@ -215,7 +216,24 @@ def test_route_rejects_bad_shapes():
     assert route(0, 10, 16392)[0] == -3
     assert route(1, -1, 64)[0] == -3
     assert route(1, 10, 64, 3)[0] == -2
-    assert route(2, 10, 64)[0] == -3
+    assert route(4, 10, 64)[0] == -3
+
+
+def test_layernorm_routes():
+    # the backward runs the row kernel and the [P, 2H] partial reduce at every T
+    for rows in (1, 64, 65, 8192, 8193, 262144):
+        for H in (256, 512, 2048, 3584, 4096, 8192, 16384):
+            st, r = route(3, rows, H, 0, 1)
+            assert st == 0 and r.kind == _lib.RMSN_KIND_BWD_ROW_DET
+            assert r.partials == r.grid >= 1
+            assert r.partial_f64 == (1 if rows > 8192 else 0)
+            need = lib.layernorm_bwd_workspace_bytes(rows, H, 0, 1)
+            assert need >= r.partials * 2 * H * (8 if r.partial_f64 else 4)
+            assert r.reduce_grid * 16 * (2 if r.partial_f64 else 4) >= 2 * H
+            assert r.vec_per_lane * r.lanes_per_row >= H // 8
+            st, f = route(2, rows, H, 0, 1)
+            assert st == 0 and f.kind == _lib.RMSN_KIND_FWD_ROW
+            assert f.vec_per_lane * f.lanes_per_row >= H // 8
 
 
 def test_route_override_selects_atomic_and_rejects_bad_knobs():

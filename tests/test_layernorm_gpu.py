@@ -1,0 +1,207 @@
+"""LayerNorm on the GPU against the FP64 oracle (``oracle.ln_*``).
+
+LayerNorm is the adjacent normalisation of the same benchmark suite (ROCm
+TransformerEngine PR "Microbenchmarking and CI performance regression test",
+benchmark_normalization table: RMSNorm and LayerNorm, forward and backward,
+M tokens x hidden, BF16, on MI355). Budgets are those of RMSNorm
+(tests/parity.py): dgamma and dbeta per element atol 1e-4 + rtol 1e-4 vs
+FP64 at the forward's FP32 statistics and at the FP64 ones; y and dx within
+one BF16 ulp of RNE(FP64) with the cancellation exemption; mean and rstd
+within relative 1e-6. The backward is fed the oracle's statistics rounded to
+FP32, so no oracle input comes from the HIP path.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import bwd_rmsnorm_fwd_02_amd as rn
+import oracle
+from tests import synth
+from tests.parity import (check_dw, check_dx, check_ln_stats, ln_dx_bound, ln_y_bound, to_f64)
+from tests.test_parity_gpu import DEV, _announce, dev_bf16, dev_f32, dev_w, host_bits
+
+pytestmark = pytest.mark.gpu
+
+SMALL = [
+    # (T, H, weight dtype, x offset, with beta)
+    (1, 8, "f32", 0.0, True), (3, 24, "bf16", 0.0, True), (64, 256, "f32", 3.0, True),
+    (65, 4096, "bf16", 0.0, False), (300, 2048, "f32", -2.0, True), (129, 6144, "bf16", 0.0, True),
+    (257, 16384, "bf16", 0.0, True), (1000, 512, "f32", 0.0, True), (2049, 1536, "bf16", 5.0, True),
+    (700, 5120, "f32", 0.0, True), (70, 1032, "bf16", 0.0, True), (33, 3584, "bf16", 1.0, True),
+    (9000, 128, "bf16", 0.0, True), (8193, 1024, "f32", 0.5, True),
+]
+
+
+def _oracle_stats(wl):
+    mu, rs, _ = oracle.ln_fwd(wl.x, wl.gamma.f64, wl.beta.f64, wl.eps, want_y=False)
+    var = 1.0 / (rs * rs) - wl.eps
+    return mu, rs, np.maximum(var, 0.0)
+
+
+@pytest.mark.parametrize("T,H,wdt,offset,with_beta", SMALL)
+def test_ln_fwd_small(T, H, wdt, offset, with_beta):
+    _announce(f"ln fwd T={T} H={H} w={wdt} offset={offset} beta={with_beta}")
+    wl = synth.make_ln(T=T, H=H, w_dtype=wdt, seed=T + 3 * H, offset=offset)
+    beta64 = wl.beta.f64 if with_beta else None
+    y, mean, rstd = rn.layernorm_fwd(dev_bf16(wl.x), dev_w(wl.gamma),
+                                     dev_w(wl.beta) if with_beta else None, wl.eps)
+    torch.cuda.synchronize()
+    mu64, rs64, y64 = oracle.ln_fwd(wl.x, wl.gamma.f64, beta64, wl.eps)
+    var64 = np.maximum(1.0 / (rs64 * rs64) - wl.eps, 0.0)
+    check_ln_stats("ln", mean.cpu().numpy(), rstd.cpu().numpy(), mu64, rs64, var64)
+    E = ln_y_bound(to_f64(wl.x), mu64, rs64, wl.gamma.f64, beta64)
+    n = check_dx("y", host_bits(y), y64, E)
+    _announce(f"  y exempted {n}")
+
+
+def _bwd(wl, det, mu32, rs32):
+    dx, dg, db = rn.layernorm_bwd(dev_bf16(wl.dy), dev_bf16(wl.x), dev_f32(mu32), dev_f32(rs32),
+                                  dev_w(wl.gamma), deterministic=det)
+    torch.cuda.synchronize()
+    return host_bits(dx), dg.cpu().numpy(), db.cpu().numpy()
+
+
+@pytest.mark.parametrize("T,H,wdt,offset,with_beta", SMALL)
+def test_ln_bwd_small(T, H, wdt, offset, with_beta):
+    _announce(f"ln bwd T={T} H={H} w={wdt} offset={offset}")
+    wl = synth.make_ln(T=T, H=H, w_dtype=wdt, seed=7 * T + H, offset=offset)
+    mu64, rs64, _ = _oracle_stats(wl)
+    mu32, rs32 = oracle.round_f32(mu64), oracle.round_f32(rs64)
+    m32, r32 = mu32.astype(np.float64), rs32.astype(np.float64)
+    dx64, c64, dg64, db64 = oracle.ln_bwd(wl.dy, wl.x, m32, r32, wl.gamma.f64)
+    _, _, dg64_i, db64_i = oracle.ln_bwd(wl.dy, wl.x, mu64, rs64, wl.gamma.f64, want_dx=False)
+    E = ln_dx_bound(to_f64(wl.x), to_f64(wl.dy), wl.gamma.f64, m32, r32, c64, H)
+    dx_d, dg_d, db_d = _bwd(wl, True, mu32, rs32)
+    n = check_dx("dx det", dx_d, dx64, E)
+    for name, got, r1, r2 in (("dgamma", dg_d, dg64, dg64_i), ("dbeta", db_d, db64, db64_i)):
+        check_dw(name + " (forward's FP32 statistics)", got, r1)
+        check_dw(name + " (FP64 statistics)", got, r2)
+    _announce(f"  dx exempted {n}")
+    dx_n, dg_n, db_n = _bwd(wl, False, mu32, rs32)
+    assert np.array_equal(dx_n, dx_d), "dx differs between modes"
+    check_dw("dgamma non-det", dg_n, dg64)
+    check_dw("dbeta non-det", db_n, db64)
+    for _ in range(3):
+        dx2, dg2, db2 = _bwd(wl, True, mu32, rs32)
+        assert np.array_equal(dx2, dx_d)
+        assert np.array_equal(dg2.view(np.uint32), dg_d.view(np.uint32))
+        assert np.array_equal(db2.view(np.uint32), db_d.view(np.uint32))
+
+
+def test_ln_zero_rows_inplace_and_errors():
+    H = 256
+    g = torch.ones(H, dtype=torch.float32, device=DEV)
+    x0 = torch.empty(0, H, dtype=torch.bfloat16, device=DEV)
+    dx, dg, db = rn.layernorm_bwd(x0, x0, torch.empty(0, device=DEV), torch.empty(0, device=DEV), g)
+    torch.cuda.synchronize()
+    assert torch.all(dg == 0) and torch.all(db == 0)
+    # y written over x, exactly in place, equals the out-of-place result
+    wl = synth.make_ln(T=333, H=H, w_dtype="f32", seed=5)
+    x = dev_bf16(wl.x)
+    y_ref, m_ref, r_ref = rn.layernorm_fwd(x, dev_w(wl.gamma), dev_w(wl.beta), wl.eps)
+    xi = x.clone()
+    rn.layernorm_fwd(xi, dev_w(wl.gamma), dev_w(wl.beta), wl.eps, y=xi)
+    torch.cuda.synchronize()
+    assert torch.equal(xi.view(torch.int16), y_ref.view(torch.int16))
+    with pytest.raises(rn.RMSNormError):
+        rn.layernorm_fwd(x[:, :250].contiguous(), g[:250], None, 1e-5)  # H not a multiple of 8
+    with pytest.raises(rn.RMSNormError):
+        rn.layernorm_fwd(x, g, None, -1.0)
+
+
+@pytest.mark.parametrize("name", list(synth.LN_CONFIGS))
+def test_ln_full_size(name):
+    _announce(f"ln full-size {name}: generating")
+    wl = synth.ln_config(name, seed=0)
+    T, H = wl.T, wl.H
+    x, dy = dev_bf16(wl.x), dev_bf16(wl.dy)
+    gam, bet = dev_w(wl.gamma), dev_w(wl.beta)
+    y, mean, rstd = rn.layernorm_fwd(x, gam, bet, wl.eps)
+    torch.cuda.synchronize()
+    _announce(f"ln full-size {name}: oracle statistics over all rows")
+    mu64, rs64, var64 = _oracle_stats(wl)
+    check_ln_stats("ln (all rows)", mean.cpu().numpy(), rstd.cpu().numpy(), mu64, rs64, var64)
+    rng = np.random.default_rng(1)
+    sample = np.unique(np.concatenate([rng.choice(T, 48, replace=False), [0, T - 1]]))
+    _, _, y64 = oracle.ln_fwd(wl.x[sample], wl.gamma.f64, wl.beta.f64, wl.eps)
+    E = ln_y_bound(to_f64(wl.x[sample]), mu64[sample], rs64[sample], wl.gamma.f64, wl.beta.f64)
+    check_dx("y (sampled rows)", host_bits(y).reshape(T, H)[sample], y64, E)
+    mu32, rs32 = oracle.round_f32(mu64), oracle.round_f32(rs64)
+    m32, r32 = mu32.astype(np.float64), rs32.astype(np.float64)
+    _announce(f"ln full-size {name}: oracle dgamma, dbeta over all rows")
+    _, _, dg64, db64 = oracle.ln_bwd(wl.dy, wl.x, m32, r32, wl.gamma.f64, want_dx=False)
+    _, _, dg64_i, db64_i = oracle.ln_bwd(wl.dy, wl.x, mu64, rs64, wl.gamma.f64, want_dx=False)
+    dx64, c64, _, _ = oracle.ln_bwd(wl.dy[sample], wl.x[sample], m32[sample], r32[sample],
+                                    wl.gamma.f64)
+    Ed = ln_dx_bound(to_f64(wl.x[sample]), to_f64(wl.dy[sample]), wl.gamma.f64, m32[sample],
+                     r32[sample], c64, H)
+    ms, rss = dev_f32(mu32), dev_f32(rs32)
+    bits = None
+    for det in (True, False):
+        dx, dg, db = rn.layernorm_bwd(dy, x, ms, rss, gam, deterministic=det)
+        torch.cuda.synchronize()
+        dxs = host_bits(dx).reshape(T, H)[sample]
+        check_dx(f"dx det={det} (sampled rows)", dxs, dx64, Ed)
+        fg = check_dw(f"dgamma det={det}", dg.cpu().numpy(), dg64)
+        fb = check_dw(f"dbeta det={det}", db.cpu().numpy(), db64)
+        check_dw(f"dgamma det={det} (FP64 statistics)", dg.cpu().numpy(), dg64_i)
+        check_dw(f"dbeta det={det} (FP64 statistics)", db.cpu().numpy(), db64_i)
+        _announce(f"  det={det}: dgamma worst {fg:.3e}, dbeta worst {fb:.3e} of budget")
+        if det:
+            bits = (dxs.copy(), dg.cpu().numpy().view(np.uint32).copy(),
+                    db.cpu().numpy().view(np.uint32).copy())
+        else:
+            assert np.array_equal(dxs, bits[0]), "dx differs between modes"
+    for i in range(5):
+        dx, dg, db = rn.layernorm_bwd(dy, x, ms, rss, gam, deterministic=True)
+        torch.cuda.synchronize()
+        assert np.array_equal(dg.cpu().numpy().view(np.uint32), bits[1]), f"run {i}"
+        assert np.array_equal(db.cpu().numpy().view(np.uint32), bits[2]), f"run {i}"
+
+
+def test_ln_step_graph_replays():
+    """forward + backward captured in one HIP graph, replayed with eager work
+    in between: every replay reproduces the eager result bit for bit."""
+    wl = synth.make_ln(T=4096, H=4096, w_dtype="bf16", seed=21)
+    x, dy = dev_bf16(wl.x), dev_bf16(wl.dy)
+    gam, bet = dev_w(wl.gamma), dev_w(wl.beta)
+    T, H = wl.T, wl.H
+    y = torch.empty_like(x)
+    mean = torch.empty(T, device=DEV)
+    rstd = torch.empty(T, device=DEV)
+    dx = torch.empty_like(x)
+    dg = torch.empty(H, device=DEV)
+    db = torch.empty(H, device=DEV)
+    ws = torch.empty(rn.layernorm_bwd_workspace_bytes(T, H, gam.dtype, True) + 256,
+                     dtype=torch.uint8, device=DEV)
+    ws = ws[(-ws.data_ptr()) % 256:]
+
+    def step():
+        rn.layernorm_fwd(x, gam, bet, wl.eps, y=y, mean=mean, rstd=rstd)
+        rn.layernorm_bwd(dy, x, mean, rstd, gam, deterministic=True, dx=dx, dgamma=dg, dbeta=db,
+                         workspace=ws)
+
+    step()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in (y, mean, rstd, dx, dg, db)]
+    g = torch.cuda.CUDAGraph()
+    cs = torch.cuda.Stream(device=DEV)
+    cs.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cs):
+        with torch.cuda.graph(g, stream=cs):
+            step()
+    torch.cuda.synchronize()
+    for i in range(3):
+        for t in (y, mean, rstd, dx, dg, db):
+            t.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for t, r in zip((y, mean, rstd, dx, dg, db), ref):
+            a = t.view(torch.int16) if t.dtype == torch.bfloat16 else t.view(torch.int32)
+            b = r.view(torch.int16) if r.dtype == torch.bfloat16 else r.view(torch.int32)
+            assert torch.equal(a, b), f"replay {i}"
+        step()
+        torch.cuda.synchronize()
