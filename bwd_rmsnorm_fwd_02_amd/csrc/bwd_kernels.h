@@ -209,8 +209,15 @@ __device__ __forceinline__ void bwd_compute(const BwdParams& p, int64_t r0, int6
 #pragma unroll
         for (int v = 0; v < NV; ++v) {
             float xf[8], dyf[8], o[8];
-            unpack8(t.x[k][v], xf);
-            unpack8(t.dy[k][v], dyf);
+            if constexpr (NV >= 4) {
+                // four vectors per lane: recompute the unpacked row rather
+                // than hold the first loop's copy across the exchange
+                unpack8(opaque(t.x[k][v]), xf);
+                unpack8(opaque(t.dy[k][v]), dyf);
+            } else {
+                unpack8(t.x[k][v], xf);
+                unpack8(t.dy[k][v], dyf);
+            }
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const float g = dyf[e] * wv[v][e];
@@ -275,7 +282,10 @@ __device__ __forceinline__ void load_weights(const BwdParams& p, int slot, int l
 // rows are loaded before the current ones are processed.
 template <int NV, int U, typename WT, bool RES, bool WIDE, int MODE, bool RC = false>
 __global__ void __launch_bounds__(WIDE ? (NV * U >= 4 ? 512 : 1024) : 256) k_bwd_row(BwdParams p) {
-    constexpr bool PF = U <= 2;
+    // Rows above 8192 elements take four vectors per lane on 512 lanes (a
+    // 1024-lane group leaves 128 registers per lane); that shape has no room
+    // for a second tile and does not prefetch.
+    constexpr bool PF = U <= 2 && NV < 4;
     extern __shared__ double lds_bwd[];
     const int tid = threadIdx.x;
     const int slot = tid / p.tpr;
@@ -499,10 +509,11 @@ static int launch_row_t(const BwdParams& p, const Route& rt, hipStream_t s) {
     return launch_row_mode<NV, U, WT, RES, false, RC>(p, rt, lds, s);
 }
 
-// (NV, U) pairs compiled: NV * U <= 8, NV <= 2.
+// (NV, U) pairs compiled: NV * U <= 8 with NV <= 2, and NV 4 with U 1.
 template <typename WT, bool RES, bool RC>
 static int launch_row_shape(const BwdParams& p, const Route& rt, hipStream_t s) {
     const int nv = rt.r.vec_per_lane, u = rt.r.unroll;
+    if (nv == 4) return u == 1 ? launch_row_t<4, 1, WT, RES, RC>(p, rt, s) : RMSN_ERR_SHAPE;
     if (nv == 1) {
         switch (u) {
             case 1: return launch_row_t<1, 1, WT, RES, RC>(p, rt, s);

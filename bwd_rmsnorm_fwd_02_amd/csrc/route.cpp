@@ -82,7 +82,7 @@ constexpr Entry kBwdTable[] = {
     {640, 1, 1, 0, 1},      // H <= 5120: one lane per vector, one row per block
     {768, 2, 2, 0, 1},      // H <= 6144
     {1024, 1, 1, 0, 1},     // H <= 8192: 1024 lanes, one row per block
-    {1 << 30, 2, 1, 0, 1},  // H <= 16384
+    {1 << 30, 4, 1, 0, 1},  // H <= 16384: 512 lanes, four vectors each
 };
 
 template <size_t N>
@@ -136,13 +136,13 @@ Shape default_ln_bwd(int nvec) { return lookup(kLnBwdTable, nvec); }
 
 // Fill the row-kernel part of a route from a shape; 0 fields take defaults.
 // The checks mirror what the kernels are compiled for: (NV, U) pairs with
-// NV * U <= 8 (the backward NV <= 2), blocks of <= 256 threads when a row
-// fits in one wave, <= 512 when NV * U >= 4, else <= 1024.
+// NV * U <= 8 (the backwards' NV 4 only with U = 1), blocks of <= 256
+// threads when a row fits in one wave, <= 512 when NV * U >= 4, else <= 1024.
 int row_shape(int op, int nvec, Shape sh, rmsn_route_t& r) {
     const int nv = sh.nv;
-    // NV 4: the forwards (ops 0, 2), and the LayerNorm backward (op 3) with U = 1
+    // NV 4: the forwards (ops 0, 2), and the backwards (ops 1, 3) with U = 1
     const bool nv_ok = nv == 1 || nv == 2 || (nv == 4 && (op == 0 || op == 2)) ||
-                       (nv == 4 && op == 3 && sh.unroll == 1);
+                       (nv == 4 && (op == 1 || op == 3) && sh.unroll == 1);
     if (!nv_ok) return RMSN_ERR_SHAPE;
     const int tpr = lanes_per_row(nvec, nv);
     if (tpr > 1024) return RMSN_ERR_SHAPE;

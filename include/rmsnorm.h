@@ -242,7 +242,7 @@ int rmsnorm_route_query(int op, int64_t rows, int64_t H, rmsn_dtype_t w_dtype,
  * route is not affected. op as for rmsnorm_route_query. Process-wide; NULL
  * clears. */
 typedef struct {
-    int vec_per_lane;   /* 1, 2 or 4 (backward: 1 or 2) */
+    int vec_per_lane;   /* 1, 2 or 4 (backward 4 only with unroll 1) */
     int unroll;         /* 1, 2 or 4; only 1 when a row spans several waves */
     int rows_per_block; /* row groups per block; block size <= 1024 */
     int blocks_per_cu;  /* grid cap = 256 * blocks_per_cu */

@@ -162,6 +162,8 @@ WIDTH_CONFIGS = {
     "w512_T1048576_bf16w": dict(T=1048576, H=512, w_dtype="bf16"),
     "w1536_T262144_f32w": dict(T=262144, H=1536, w_dtype="f32"),
     "w5120_T65536_bf16w": dict(T=65536, H=5120, w_dtype="bf16"),
+    # the widest shape of the TE page's normalization table (8192 x 16384)
+    "w16384_T8192_bf16w": dict(T=8192, H=16384, w_dtype="bf16"),
 }
 
 

@@ -249,6 +249,11 @@ def test_route_override_selects_atomic_and_rejects_bad_knobs():
         # knobs the kernels cannot honour make the route fail (no launch)
         assert lib.rmsnorm_route_override(1, ctypes.byref(K(3, 0, 0, 0, 0, 0))) == 0
         assert route(1, 131072, 2048, 1, 1)[0] == -3
+        assert lib.rmsnorm_route_override(1, ctypes.byref(K(4, 2, 0, 0, 0, 0))) == 0
+        assert route(1, 4096, 16384, 1, 1)[0] == -3    # backward NV 4 is compiled for U = 1
+        assert lib.rmsnorm_route_override(1, ctypes.byref(K(4, 1, 0, 0, 0, 0))) == 0
+        st, r = route(1, 4096, 16384, 1, 1)
+        assert st == 0 and r.vec_per_lane == 4 and r.lanes_per_row == 512
         assert lib.rmsnorm_route_override(1, ctypes.byref(K(2, 8, 0, 0, 0, 0))) == 0
         assert route(1, 4096, 4096, 0, 1)[0] == -3     # NV * U > 8 is not compiled
         assert lib.rmsnorm_route_override(1, ctypes.byref(K(1, 8, 2, 0, 0, 0))) == 0
