@@ -3,21 +3,20 @@
 
 namespace rmsn {
 
-// Fixed-order reduction of P partial rows of W columns. A block owns 128
-// contiguous bytes of columns (8 chunks of 16 bytes, so every partial row is
-// read with whole cache lines) and S = blockDim/8 slices: thread (chunk c,
-// slice s) sums partial rows s, s + S, s + 2S, ... in increasing order, four
-// loads in flight at a time. The slice sums are then added in a fixed order:
-// a butterfly over the 8 slices each wave holds, then the waves in index
-// order. Nothing depends on timing, so the result is bit-reproducible.
-// Columns below `split` go to out0, the others to out1 (LayerNorm's dgamma
-// and dbeta share one partial row); split is a multiple of the chunk width.
-template <typename PT>
+// Fixed-order reduction of P partial rows of W columns. A block owns CC * 16
+// contiguous bytes of columns (CC chunks of 16 bytes) and S = blockDim/CC
+// slices: thread (chunk c, slice s) sums partial rows s, s + S, s + 2S, ...
+// in increasing order, four loads in flight at a time. The slice sums are
+// then added in a fixed order: a butterfly over the slices each wave holds,
+// then the waves in index order. Nothing depends on timing, so the result is
+// bit-reproducible. Columns below `split` go to out0, the others to out1
+// (LayerNorm's dgamma and dbeta share one partial row); split is a multiple
+// of the chunk width.
+template <typename PT, int CC>
 __global__ void __launch_bounds__(1024) k_dw_reduce(const PT* __restrict__ part, int64_t P,
                                                     int32_t H, float* __restrict__ dw,
                                                     float* __restrict__ out1, int32_t split) {
     constexpr int CPC = 16 / sizeof(PT);  // columns per 16-byte chunk
-    constexpr int CC = 8;                 // chunks per block
     __shared__ double sm_red[16][CC * CPC];
     const int S = blockDim.x / CC;
     const int cc = threadIdx.x % CC;
@@ -57,12 +56,12 @@ __global__ void __launch_bounds__(1024) k_dw_reduce(const PT* __restrict__ part,
                 for (int e = 0; e < CPC; ++e) a[e] += (double)v[u][e];
         }
     }
-    // butterfly over the wave's 8 slices (lane bits 3..5), fixed pairing
+    // butterfly over the wave's 64 / CC slices (the lane bits above the
+    // chunk index), fixed pairing
 #pragma unroll
     for (int e = 0; e < CPC; ++e) {
-        a[e] += __shfl_xor(a[e], 8, 64);
-        a[e] += __shfl_xor(a[e], 16, 64);
-        a[e] += __shfl_xor(a[e], 32, 64);
+#pragma unroll
+        for (int m = CC; m < 64; m <<= 1) a[e] += __shfl_xor(a[e], m, 64);
     }
     const int wave = threadIdx.x >> 6;
     const int nwaves = blockDim.x >> 6;
@@ -97,12 +96,15 @@ int launch_col_reduce(const void* partial, const Route& rt, int32_t W, float* ou
     const unsigned threads = (unsigned)rt.r.reduce_threads;
     dim3 grid((unsigned)rt.r.reduce_grid), block(threads);
     const size_t lds = 0;
+    // the route sizes the grid for 16-byte chunks per block (kReduceChunks)
     if (rt.r.partial_f64)
-        launch_kernel(k_dw_reduce<double>, grid, block, lds, s, static_cast<const double*>(partial),
-                      (int64_t)rt.r.partials, W, out0, out1, split);
+        launch_kernel((k_dw_reduce<double, kReduceChunks>), grid, block, lds, s,
+                      static_cast<const double*>(partial), (int64_t)rt.r.partials, W, out0, out1,
+                      split);
     else
-        launch_kernel(k_dw_reduce<float>, grid, block, lds, s, static_cast<const float*>(partial),
-                      (int64_t)rt.r.partials, W, out0, out1, split);
+        launch_kernel((k_dw_reduce<float, kReduceChunks>), grid, block, lds, s,
+                      static_cast<const float*>(partial), (int64_t)rt.r.partials, W, out0, out1,
+                      split);
     return hipGetLastError() == hipSuccess ? RMSN_OK : RMSN_ERR_LAUNCH;
 }
 

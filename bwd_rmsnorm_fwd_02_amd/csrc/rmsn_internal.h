@@ -17,6 +17,10 @@ constexpr int64_t kMaxH = 16384;
 // The partition of rows into dw partials is derived from this fixed CU count,
 // never from the device, so deterministic dw bits do not depend on the part.
 constexpr int kPartitionCUs = 256;
+// 16-byte column chunks per block of the dw column reduce (128 bytes of
+// columns per block; 4 and 16 chunks measured slower at 4096 x 4096 and
+// 32768 x 4 x 256).
+constexpr int kReduceChunks = 8;
 
 // Backward forms: plain rows, fused residual (h, optional dres), or plain
 // rows with rstd recomputed from x inside the backward.

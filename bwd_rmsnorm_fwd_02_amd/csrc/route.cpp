@@ -242,7 +242,7 @@ int route(int op, int64_t rows, int64_t H, rmsn_dtype_t wdt, int det, int form, 
         if (k && k->partial_f64) r.partial_f64 = k->partial_f64 == 1 ? 1 : 0;
         r.partials = r.grid;
         const int psize = r.partial_f64 ? 8 : 4;
-        r.reduce_grid = ceil_div(2 * H * psize, 128);
+        r.reduce_grid = ceil_div(2 * H * psize, 16 * kReduceChunks);
         r.reduce_threads = 1024;
         out->workspace = align256((size_t)r.partials * (size_t)(2 * H) * psize);
         (void)det;
@@ -308,7 +308,7 @@ int route(int op, int64_t rows, int64_t H, rmsn_dtype_t wdt, int det, int form, 
         if (k && k->partial_f64) r.partial_f64 = k->partial_f64 == 1 ? 1 : 0;
         r.partials = r.grid;
         const int psize = r.partial_f64 ? 8 : 4;
-        r.reduce_grid = ceil_div(H * psize, 128);
+        r.reduce_grid = ceil_div(H * psize, 16 * kReduceChunks);
         r.reduce_threads = 1024;  // 128 slices: one round of loads up to P = 512
         out->workspace = align256((size_t)r.partials * (size_t)H * psize);
     } else {
