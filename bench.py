@@ -349,8 +349,15 @@ def bench_layernorm(args, np, torch, rn, _lib, lib, synth, dev, d16) -> int:
     config = {"workload": args.config, "norm": "layernorm", "op": op, "T": T, "H": H,
               "w_dtype": wl.gamma.dtype, "deterministic": True, "global_batch": T, "seq_len": T,
               "parallelism": "none (1 GPU)", "buffer_sets": n_sets}
+    traffic = None
+    tr_path = os.path.join(ROOT, "profiles", f"traffic_{args.config}.json")
+    if os.path.exists(tr_path) and op == "fwd+bwd":
+        from bwd_rmsnorm_fwd_02_amd import build as _b
+        rec = json.load(open(tr_path))
+        if rec.get("source_hash") == _b.source_hash() and t["dom_name"] in rec.get("kernels", {}):
+            traffic = rec["kernels"][t["dom_name"]]["bytes_per_launch"]
     out = result_line(args, f"LayerNorm {op} effective HBM GB/s, per (T,H)", op, t["value"], t,
-                      step_bytes, config, None, cpu)
+                      step_bytes, config, traffic, cpu)
     print(json.dumps(out), flush=True)
     return 0
 
