@@ -185,7 +185,7 @@ __global__ void __launch_bounds__(WIDE ? (NV * U >= 4 ? 512 : 1024) : 256) k_fwd
             for (int v = 0; v < NV; ++v) {
                 if (!vok[v]) continue;
                 const int64_t c = (int64_t)(lr + v * p.tpr) * kVec;
-                if constexpr (RES) st16(p.h + oh + c, hout[k][v]);
+                if constexpr (RES) st16_stream(p.h + oh + c, hout[k][v]);
                 st16_stream(p.y + oy + c, yout[k][v]);
             }
         }
