@@ -55,7 +55,7 @@ class RouteInfo(ctypes.Structure):
                 ("unroll", ctypes.c_int), ("block_threads", ctypes.c_int),
                 ("partial_f64", ctypes.c_int), ("reduce_threads", ctypes.c_int),
                 ("grid", ctypes.c_int64), ("partials", ctypes.c_int64),
-                ("reduce_grid", ctypes.c_int64)]
+                ("reduce_grid", ctypes.c_int64), ("stream_loads", ctypes.c_int)]
 
     def as_dict(self):
         return {f: getattr(self, f) for f, _ in self._fields_}
@@ -64,7 +64,8 @@ class RouteInfo(ctypes.Structure):
 class RouteKnobs(ctypes.Structure):
     _fields_ = [("vec_per_lane", ctypes.c_int), ("unroll", ctypes.c_int),
                 ("rows_per_block", ctypes.c_int), ("blocks_per_cu", ctypes.c_int),
-                ("partial_f64", ctypes.c_int), ("kind", ctypes.c_int)]
+                ("partial_f64", ctypes.c_int), ("kind", ctypes.c_int),
+                ("stream_loads", ctypes.c_int)]
 
 
 class RMSNormError(RuntimeError):

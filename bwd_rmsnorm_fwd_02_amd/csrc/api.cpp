@@ -180,7 +180,8 @@ int fwd_impl(const void* x, const rmsn_view_t& xv, const void* r, const rmsn_vie
     }
 
     Route rt;
-    if ((st = route(0, rows, xv.H, wdt, 1, kFormPlain, &rt)) != RMSN_OK) return st;
+    if ((st = route(0, rows, xv.H, wdt, 1, residual ? kFormResidual : kFormPlain, &rt)) != RMSN_OK)
+        return st;
     FwdParams p;
     memset(&p, 0, sizeof p);
     p.x = static_cast<const uint16_t*>(x);
@@ -561,7 +562,7 @@ int rmsnorm_route_query(int op, int64_t rows, int64_t H, rmsn_dtype_t w_dtype, i
                         int form, rmsn_route_t* out) {
     if (!out) return RMSN_ERR_NULL;
     Route rt;
-    const int st = route(op, rows, H, w_dtype, deterministic, op == 1 ? form : kFormPlain, &rt);
+    const int st = route(op, rows, H, w_dtype, deterministic, op <= 1 ? form : kFormPlain, &rt);
     *out = rt.r;
     return st;
 }

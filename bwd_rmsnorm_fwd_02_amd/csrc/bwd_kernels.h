@@ -58,7 +58,8 @@ struct BwdTile {
 // around memory operations (branches there make the compiler's wait counting
 // fall back to waiting for everything). Without a residual gradient the dres
 // slot reloads dy, which stays unused.
-template <int NV, int U, bool RES, bool RC = false>
+// NT: 0 plain loads, 1 stream dy (and dres), 2 stream x too.
+template <int NV, int U, bool RES, bool RC = false, int NT = 0>
 __device__ __forceinline__ void bwd_load(const BwdParams& p, int64_t r0, int64_t rend, int slot,
                                          int lr, BwdTile<NV, U, RES>& t) {
 #pragma unroll
@@ -82,9 +83,9 @@ __device__ __forceinline__ void bwd_load(const BwdParams& p, int64_t r0, int64_t
             int vi = lr + v * p.tpr;
             if (vi > p.nvec - 1) vi = p.nvec - 1;
             const int64_t c = (int64_t)vi * kVec;
-            t.x[k][v] = ld16(p.x + ox + c);
-            t.dy[k][v] = ld16(p.dy + ody + c);
-            if constexpr (RES) t.dres[k][v] = ld16(rsrc + ores + c);
+            t.x[k][v] = ld16p<(NT >= 2)>(p.x + ox + c);
+            t.dy[k][v] = ld16p<(NT >= 1)>(p.dy + ody + c);
+            if constexpr (RES) t.dres[k][v] = ld16p<(NT >= 1)>(rsrc + ores + c);
         }
         if constexpr (!RC) t.rs[k] = p.rstd[r];
     }
@@ -280,7 +281,7 @@ __device__ __forceinline__ void load_weights(const BwdParams& p, int slot, int l
 // Large-T row kernel: dx for the block's rows plus the block's dw sums.
 // Each iteration a row group takes U rows; with U <= 2 the next iteration's
 // rows are loaded before the current ones are processed.
-template <int NV, int U, typename WT, bool RES, bool WIDE, int MODE, bool RC = false>
+template <int NV, int U, typename WT, bool RES, bool WIDE, int MODE, bool RC = false, int NT = 0>
 __global__ void __launch_bounds__(WIDE ? (NV * U >= 4 ? 512 : 1024) : 256) k_bwd_row(BwdParams p) {
     // Rows above 8192 elements take four vectors per lane on 512 lanes (a
     // 1024-lane group leaves 128 registers per lane); that shape has no room
@@ -321,11 +322,11 @@ __global__ void __launch_bounds__(WIDE ? (NV * U >= 4 ? 512 : 1024) : 256) k_bwd
     if (r0 < rend) {
         BwdTile<NV, U, RES> cur;
         BwdTile<NV, PF ? U : 1, RES> nxt;
-        bwd_load<NV, U, RES, RC>(p, r0, rend, slot, lr, cur);
+        bwd_load<NV, U, RES, RC, NT>(p, r0, rend, slot, lr, cur);
         bwd_ready<NV, U, RES, RC>(cur);
 #pragma unroll 1
         for (; r0 < rend; r0 += stride) {
-            if constexpr (PF) bwd_load<NV, U, RES, RC>(p, r0 + stride, rend, slot, lr, nxt);
+            if constexpr (PF) bwd_load<NV, U, RES, RC, NT>(p, r0 + stride, rend, slot, lr, nxt);
             uint4 out[U][NV];
             bwd_compute<NV, U, RES, WIDE, true, RC>(p, r0, rend, slot, lr, wv, vok, cur, acc, out, red,
                                                     redd, buf);
@@ -337,7 +338,7 @@ __global__ void __launch_bounds__(WIDE ? (NV * U >= 4 ? 512 : 1024) : 256) k_bwd
             }
             bwd_store<NV, U>(p, r0, rend, slot, lr, vok, out);
             if constexpr (!PF) {
-                if (r0 + stride < rend) bwd_load<NV, U, RES, RC>(p, r0 + stride, rend, slot, lr, cur);
+                if (r0 + stride < rend) bwd_load<NV, U, RES, RC, NT>(p, r0 + stride, rend, slot, lr, cur);
             }
         }
     }
@@ -486,20 +487,30 @@ inline size_t bwd_row_lds_bytes(const rmsn_route_t& r, int H, bool rc) {
     return lds;
 }
 
-template <int NV, int U, typename WT, bool RES, bool WIDE, bool RC>
-static int launch_row_mode(const BwdParams& p, const Route& rt, size_t lds, hipStream_t s) {
+template <int NV, int U, typename WT, bool RES, bool WIDE, bool RC, int NT>
+static int launch_row_nt(const BwdParams& p, const Route& rt, size_t lds, hipStream_t s) {
     dim3 grid((unsigned)rt.r.grid), block((unsigned)rt.r.block_threads);
     if (rt.r.kind == RMSN_KIND_BWD_ROW_ATOMIC) {
         if constexpr (NV == 1 && U <= 2)
-            launch_kernel((k_bwd_row<NV, U, WT, RES, WIDE, kModeAtomic, RC>), grid, block, lds, s, p);
+            launch_kernel((k_bwd_row<NV, U, WT, RES, WIDE, kModeAtomic, RC, NT>), grid, block, lds, s, p);
         else
             return RMSN_ERR_SHAPE;
     } else if (rt.r.partial_f64) {
-        launch_kernel((k_bwd_row<NV, U, WT, RES, WIDE, kModePartF64, RC>), grid, block, lds, s, p);
+        launch_kernel((k_bwd_row<NV, U, WT, RES, WIDE, kModePartF64, RC, NT>), grid, block, lds, s, p);
     } else {
-        launch_kernel((k_bwd_row<NV, U, WT, RES, WIDE, kModePartF32, RC>), grid, block, lds, s, p);
+        launch_kernel((k_bwd_row<NV, U, WT, RES, WIDE, kModePartF32, RC, NT>), grid, block, lds, s, p);
     }
     return hipGetLastError() == hipSuccess ? RMSN_OK : RMSN_ERR_LAUNCH;
+}
+
+template <int NV, int U, typename WT, bool RES, bool WIDE, bool RC>
+static int launch_row_mode(const BwdParams& p, const Route& rt, size_t lds, hipStream_t s) {
+    switch (rt.r.stream_loads) {
+        case 0: return launch_row_nt<NV, U, WT, RES, WIDE, RC, 0>(p, rt, lds, s);
+        case 1: return launch_row_nt<NV, U, WT, RES, WIDE, RC, 1>(p, rt, lds, s);
+        case 2: return launch_row_nt<NV, U, WT, RES, WIDE, RC, 2>(p, rt, lds, s);
+        default: return RMSN_ERR_SHAPE;
+    }
 }
 
 template <int NV, int U, typename WT, bool RES, bool RC>

@@ -35,7 +35,7 @@ struct FwdTile {
 // row end are clamped to the last valid ones and their values ignored, so
 // there are no branches around memory operations (branches there make the
 // compiler's wait counting fall back to waiting for everything).
-template <int NV, int U, bool RES>
+template <int NV, int U, bool RES, bool NTX>
 __device__ __forceinline__ void fwd_load(const FwdParams& p, int64_t r0, int slot, int lr,
                                          FwdTile<NV, U, RES>& t) {
 #pragma unroll
@@ -50,8 +50,8 @@ __device__ __forceinline__ void fwd_load(const FwdParams& p, int64_t r0, int slo
             int vi = lr + v * p.tpr;
             if (vi > p.nvec - 1) vi = p.nvec - 1;
             const int64_t c = (int64_t)vi * kVec;
-            t.x[k][v] = ld16(p.x + ox + c);
-            if constexpr (RES) t.r[k][v] = ld16(p.r + orr + c);
+            t.x[k][v] = ld16p<NTX>(p.x + ox + c);
+            if constexpr (RES) t.r[k][v] = ld16p<NTX>(p.r + orr + c);
         }
     }
 }
@@ -67,7 +67,8 @@ __device__ __forceinline__ void fwd_ready(const FwdTile<NV, U, RES>& t) {
         }
 }
 
-template <int NV, int U, typename WT, bool RES, bool WIDE>
+// NTX: stream (non-temporal) the loads of x and r.
+template <int NV, int U, typename WT, bool RES, bool WIDE, bool NTX>
 __global__ void __launch_bounds__(WIDE ? (NV * U >= 4 ? 512 : 1024) : 256) k_fwd(FwdParams p) {
     constexpr bool PF = U <= 2;  // software-pipeline the next iteration's rows
     extern __shared__ double lds_fwd[];
@@ -97,12 +98,12 @@ __global__ void __launch_bounds__(WIDE ? (NV * U >= 4 ? 512 : 1024) : 256) k_fwd
     if (r0 >= p.rows) return;  // whole block idle (uniform)
     FwdTile<NV, U, RES> cur;
     FwdTile<NV, PF ? U : 1, RES> nxt;
-    fwd_load<NV, U, RES>(p, r0, slot, lr, cur);
+    fwd_load<NV, U, RES, NTX>(p, r0, slot, lr, cur);
     fwd_ready<NV, U, RES>(cur);
     int buf = 0;
 #pragma unroll 1
     for (; r0 < p.rows; r0 += stride) {
-        if constexpr (PF) fwd_load<NV, U, RES>(p, r0 + stride, slot, lr, nxt);
+        if constexpr (PF) fwd_load<NV, U, RES, NTX>(p, r0 + stride, slot, lr, nxt);
 
         // compute: h (residual), sum of squares, row sums, outputs in registers
         double acc[U];
@@ -190,7 +191,7 @@ __global__ void __launch_bounds__(WIDE ? (NV * U >= 4 ? 512 : 1024) : 256) k_fwd
             }
         }
         if constexpr (!PF) {
-            if (r0 + stride < p.rows) fwd_load<NV, U, RES>(p, r0 + stride, slot, lr, cur);
+            if (r0 + stride < p.rows) fwd_load<NV, U, RES, NTX>(p, r0 + stride, slot, lr, cur);
         }
     }
 }
@@ -206,10 +207,14 @@ static int launch_fwd_t(const FwdParams& p, const Route& rt, hipStream_t s) {
     const rmsn_route_t& r = rt.r;
     const size_t lds = fwd_lds_bytes(r);
     dim3 grid((unsigned)r.grid), block((unsigned)r.block_threads);
-    if (r.lanes_per_row > 64)
-        launch_kernel((k_fwd<NV, U, WT, RES, true>), grid, block, lds, s, p);
-    else
-        launch_kernel((k_fwd<NV, U, WT, RES, false>), grid, block, lds, s, p);
+    const bool ntx = r.stream_loads >= 2;
+    if (r.lanes_per_row > 64) {
+        if (ntx) launch_kernel((k_fwd<NV, U, WT, RES, true, true>), grid, block, lds, s, p);
+        else launch_kernel((k_fwd<NV, U, WT, RES, true, false>), grid, block, lds, s, p);
+    } else {
+        if (ntx) launch_kernel((k_fwd<NV, U, WT, RES, false, true>), grid, block, lds, s, p);
+        else launch_kernel((k_fwd<NV, U, WT, RES, false, false>), grid, block, lds, s, p);
+    }
     return hipGetLastError() == hipSuccess ? RMSN_OK : RMSN_ERR_LAUNCH;
 }
 

@@ -45,6 +45,18 @@ __device__ __forceinline__ uint4 ld16(const uint16_t* p) {
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
+// 16-byte load with a cache policy: NT marks it non-temporal (streamed), for
+// inputs that no later access in the step will find in the caches anyway.
+template <bool NT>
+__device__ __forceinline__ uint4 ld16p(const uint16_t* p) {
+    if constexpr (NT) {
+        const u32x4 w = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+        return make_uint4(w.x, w.y, w.z, w.w);
+    } else {
+        return ld16(p);
+    }
+}
+
 // Streaming store for the large outputs (y, dx, and the residual form's h):
 // marked non-temporal so they do not displace inputs from the caches, and so
 // that a step's forward leaves less dirty data to drain while the backward

@@ -221,12 +221,14 @@ typedef struct {
     int64_t grid;        /* blocks of the main kernel */
     int64_t partials;    /* dw partial rows written (0 if none) */
     int64_t reduce_grid; /* blocks of the dw reduce (column-task blocks for small T) */
+    int stream_loads;    /* RMSNorm row kernels' loads: 0 plain, 1 dy/dres non-temporal,
+                            2 all inputs non-temporal (a function of the shape) */
 } rmsn_route_t;
 
 /* The route table: which kernel and launch shape serve this problem.
  * op: 0 forward, 1 backward, 2 LayerNorm forward, 3 LayerNorm backward.
- * form (op 1 only; ignored otherwise): 0 plain (rmsnorm_bwd,
- * rmsnorm_bwd_strided), 1 residual (rmsnorm_residual_bwd), 2 recompute
+ * form (ops 0 and 1; ignored otherwise): 0 plain (rmsnorm_fwd*, rmsnorm_bwd,
+ * rmsnorm_bwd_strided), 1 residual (rmsnorm_residual_fwd/bwd), 2 recompute
  * (rmsnorm_bwd_recompute).
  * Pure host function; needs no GPU.
  * Returns RMSN_OK or RMSN_ERR_SHAPE / RMSN_ERR_DTYPE / RMSN_ERR_NULL. */
@@ -248,6 +250,7 @@ typedef struct {
     int blocks_per_cu;  /* grid cap = 256 * blocks_per_cu */
     int partial_f64;    /* backward: 1 FP64 partials, 2 FP32 partials */
     int kind;           /* backward: RMSN_KIND_BWD_ROW_DET or RMSN_KIND_BWD_ROW_ATOMIC */
+    int stream_loads;   /* 1 + the stream_loads level to force (0 keeps the route's) */
 } rmsn_route_knobs_t;
 int rmsnorm_route_override(int op, const rmsn_route_knobs_t* knobs);
 
