@@ -41,7 +41,7 @@ struct LnFwdTile {
     uint4 x[U][NV];
 };
 
-template <int NV, int U>
+template <int NV, int U, bool NTX>
 __device__ __forceinline__ void ln_fwd_load(const LnFwdParams& p, int64_t r0, int slot, int lr,
                                             LnFwdTile<NV, U>& t) {
 #pragma unroll
@@ -52,7 +52,7 @@ __device__ __forceinline__ void ln_fwd_load(const LnFwdParams& p, int64_t r0, in
         for (int v = 0; v < NV; ++v) {
             int vi = lr + v * p.tpr;
             if (vi > p.nvec - 1) vi = p.nvec - 1;
-            t.x[k][v] = ld16(p.x + r * p.H + (int64_t)vi * kVec);
+            t.x[k][v] = ld16p<NTX>(p.x + r * p.H + (int64_t)vi * kVec);
         }
     }
 }
@@ -93,7 +93,8 @@ __device__ __forceinline__ void ln_row_sums_d(double (&v)[U], int tpr, int rpb, 
     }
 }
 
-template <int NV, int U, typename WT, bool WIDE>
+// NTX: stream (non-temporal) the loads of x.
+template <int NV, int U, typename WT, bool WIDE, bool NTX>
 __global__ void __launch_bounds__(WIDE ? (NV * U >= 4 ? 512 : 1024) : 256) k_ln_fwd(LnFwdParams p) {
     constexpr bool PF = U <= 2;
     extern __shared__ double lds_lnf[];
@@ -128,12 +129,12 @@ __global__ void __launch_bounds__(WIDE ? (NV * U >= 4 ? 512 : 1024) : 256) k_ln_
     if (r0 >= p.rows) return;  // whole block idle (uniform)
     LnFwdTile<NV, U> cur;
     LnFwdTile<NV, PF ? U : 1> nxt;
-    ln_fwd_load<NV, U>(p, r0, slot, lr, cur);
+    ln_fwd_load<NV, U, NTX>(p, r0, slot, lr, cur);
     ln_fwd_ready<NV, U>(cur);
     int buf = 0;
 #pragma unroll 1
     for (; r0 < p.rows; r0 += stride) {
-        if constexpr (PF) ln_fwd_load<NV, U>(p, r0 + stride, slot, lr, nxt);
+        if constexpr (PF) ln_fwd_load<NV, U, NTX>(p, r0 + stride, slot, lr, nxt);
 
         // pass 1: mean
         double s1[U];
@@ -210,7 +211,7 @@ __global__ void __launch_bounds__(WIDE ? (NV * U >= 4 ? 512 : 1024) : 256) k_ln_
             }
         }
         if constexpr (!PF) {
-            if (r0 + stride < p.rows) ln_fwd_load<NV, U>(p, r0 + stride, slot, lr, cur);
+            if (r0 + stride < p.rows) ln_fwd_load<NV, U, NTX>(p, r0 + stride, slot, lr, cur);
         }
     }
 }
@@ -225,7 +226,8 @@ struct LnBwdTile {
     float rs[U];
 };
 
-template <int NV, int U>
+// NT: 0 plain loads, 1 stream dy, 2 stream x too.
+template <int NV, int U, int NT>
 __device__ __forceinline__ void ln_bwd_load(const LnBwdParams& p, int64_t r0, int slot, int lr,
                                             LnBwdTile<NV, U>& t) {
 #pragma unroll
@@ -237,8 +239,8 @@ __device__ __forceinline__ void ln_bwd_load(const LnBwdParams& p, int64_t r0, in
             int vi = lr + v * p.tpr;
             if (vi > p.nvec - 1) vi = p.nvec - 1;
             const int64_t o = r * p.H + (int64_t)vi * kVec;
-            t.x[k][v] = ld16(p.x + o);
-            t.dy[k][v] = ld16(p.dy + o);
+            t.x[k][v] = ld16p<(NT >= 2)>(p.x + o);
+            t.dy[k][v] = ld16p<(NT >= 1)>(p.dy + o);
         }
         t.mu[k] = p.mean[r];
         t.rs[k] = p.rstd[r];
@@ -301,7 +303,7 @@ __device__ __forceinline__ void ln_row_sums2(float (&a)[U], float (&b)[U], int t
     }
 }
 
-template <int NV, int U, typename WT, bool WIDE, bool F64>
+template <int NV, int U, typename WT, bool WIDE, bool F64, int NT>
 __global__ void __launch_bounds__(WIDE ? (NV * U >= 4 ? 512 : 1024) : 256)
     k_ln_bwd_row(LnBwdParams p) {
     // Rows of more than 8192 elements take 512 lanes with four vectors each
@@ -349,11 +351,11 @@ __global__ void __launch_bounds__(WIDE ? (NV * U >= 4 ? 512 : 1024) : 256)
     if (r0 < p.rows) {
         LnBwdTile<NV, U> cur;
         LnBwdTile<NV, PF ? U : 1> nxt;
-        ln_bwd_load<NV, U>(p, r0, slot, lr, cur);
+        ln_bwd_load<NV, U, NT>(p, r0, slot, lr, cur);
         ln_bwd_ready<NV, U>(cur);
 #pragma unroll 1
         for (; r0 < p.rows; r0 += stride) {
-            if constexpr (PF) ln_bwd_load<NV, U>(p, r0 + stride, slot, lr, nxt);
+            if constexpr (PF) ln_bwd_load<NV, U, NT>(p, r0 + stride, slot, lr, nxt);
             float s1[U], s2[U];
 #pragma unroll
             for (int k = 0; k < U; ++k) {
@@ -430,7 +432,7 @@ __global__ void __launch_bounds__(WIDE ? (NV * U >= 4 ? 512 : 1024) : 256)
                 }
             }
             if constexpr (!PF) {
-                if (r0 + stride < p.rows) ln_bwd_load<NV, U>(p, r0 + stride, slot, lr, cur);
+                if (r0 + stride < p.rows) ln_bwd_load<NV, U, NT>(p, r0 + stride, slot, lr, cur);
             }
         }
     }
@@ -509,10 +511,14 @@ template <int NV, int U, typename WT>
 static int launch_ln_fwd_t(const LnFwdParams& p, const Route& rt, hipStream_t s) {
     const size_t lds = ln_fwd_lds_bytes(rt.r);
     dim3 grid((unsigned)rt.r.grid), block((unsigned)rt.r.block_threads);
-    if (rt.r.lanes_per_row > 64)
-        launch_kernel((k_ln_fwd<NV, U, WT, true>), grid, block, lds, s, p);
-    else
-        launch_kernel((k_ln_fwd<NV, U, WT, false>), grid, block, lds, s, p);
+    const bool ntx = rt.r.stream_loads >= 2;
+    if (rt.r.lanes_per_row > 64) {
+        if (ntx) launch_kernel((k_ln_fwd<NV, U, WT, true, true>), grid, block, lds, s, p);
+        else launch_kernel((k_ln_fwd<NV, U, WT, true, false>), grid, block, lds, s, p);
+    } else {
+        if (ntx) launch_kernel((k_ln_fwd<NV, U, WT, false, true>), grid, block, lds, s, p);
+        else launch_kernel((k_ln_fwd<NV, U, WT, false, false>), grid, block, lds, s, p);
+    }
     return hipGetLastError() == hipSuccess ? RMSN_OK : RMSN_ERR_LAUNCH;
 }
 
@@ -529,14 +535,24 @@ static int launch_ln_fwd_wt(const LnFwdParams& p, const Route& rt, hipStream_t s
     return RMSN_ERR_SHAPE;
 }
 
-template <int NV, int U, typename WT, bool WIDE>
-static int launch_ln_bwd_mode(const LnBwdParams& p, const Route& rt, size_t lds, hipStream_t s) {
+template <int NV, int U, typename WT, bool WIDE, int NT>
+static int launch_ln_bwd_nt(const LnBwdParams& p, const Route& rt, size_t lds, hipStream_t s) {
     dim3 grid((unsigned)rt.r.grid), block((unsigned)rt.r.block_threads);
     if (rt.r.partial_f64)
-        launch_kernel((k_ln_bwd_row<NV, U, WT, WIDE, true>), grid, block, lds, s, p);
+        launch_kernel((k_ln_bwd_row<NV, U, WT, WIDE, true, NT>), grid, block, lds, s, p);
     else
-        launch_kernel((k_ln_bwd_row<NV, U, WT, WIDE, false>), grid, block, lds, s, p);
+        launch_kernel((k_ln_bwd_row<NV, U, WT, WIDE, false, NT>), grid, block, lds, s, p);
     return hipGetLastError() == hipSuccess ? RMSN_OK : RMSN_ERR_LAUNCH;
+}
+
+template <int NV, int U, typename WT, bool WIDE>
+static int launch_ln_bwd_mode(const LnBwdParams& p, const Route& rt, size_t lds, hipStream_t s) {
+    switch (rt.r.stream_loads) {
+        case 0: return launch_ln_bwd_nt<NV, U, WT, WIDE, 0>(p, rt, lds, s);
+        case 1: return launch_ln_bwd_nt<NV, U, WT, WIDE, 1>(p, rt, lds, s);
+        case 2: return launch_ln_bwd_nt<NV, U, WT, WIDE, 2>(p, rt, lds, s);
+        default: return RMSN_ERR_SHAPE;
+    }
 }
 
 template <int NV, int U, typename WT>

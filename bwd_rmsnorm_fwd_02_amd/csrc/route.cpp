@@ -37,10 +37,11 @@ constexpr size_t kMaxLds = 64 * 1024;
 // MI355X's Infinity Cache (the memory-side cache behind the L2s).
 constexpr double kMallBytes = 256.0 * 1024 * 1024;
 
-// Cache policy of the RMSNorm row kernels' loads, a function of the shape
-// only. When the forward's tensors (x and y, plus r and h in the residual
-// form) exceed the Infinity Cache, nothing it read survives to the
-// backward, so every large input is loaded non-temporally (2). Otherwise x
+// Cache policy of the row kernels' loads (RMSNorm and LayerNorm), a
+// function of the shape only. When the forward's tensors (x and y, plus r
+// and h in the residual form) fill the Infinity Cache, nothing it read
+// survives to the backward, so every large input is loaded non-temporally
+// (2). Otherwise x
 // can still be found by the backward: from 32M elements only the tensors
 // read once (dy, dres) are streamed (1), which keeps them from evicting x;
 // below that (0) plain loads measured no faster. Step times against plain
@@ -51,7 +52,7 @@ constexpr double kMallBytes = 256.0 * 1024 * 1024;
 int stream_level(int64_t rows, int64_t H, bool residual) {
     const double e = (double)rows * (double)H;
     const double fwd_bytes = e * 2.0 * (residual ? 4.0 : 2.0);
-    if (fwd_bytes > kMallBytes) return 2;
+    if (fwd_bytes >= kMallBytes) return 2;
     if (e >= 32.0 * 1024 * 1024) return 1;
     return 0;
 }
@@ -237,6 +238,8 @@ int route(int op, int64_t rows, int64_t H, rmsn_dtype_t wdt, int det, int form, 
         if (!((nv == 1 && u <= 2) || (nv == 2 && u <= 4 && u != 3) || (nv == 4 && u == 1)))
             return RMSN_ERR_SHAPE;
         r.kind = RMSN_KIND_FWD_ROW;
+        r.stream_loads = stream_level(rows, H, false);
+        if (g_have_knobs[2] && g_knobs[2].stream_loads) r.stream_loads = g_knobs[2].stream_loads - 1;
         const int bpc = sh.bpc > 0 ? sh.bpc : (2048 / r.block_threads > 0 ? 2048 / r.block_threads : 1);
         const int64_t cap = (int64_t)kPartitionCUs * bpc;
         const int64_t g = ceil_div(rows, (int64_t)r.rows_per_block * r.unroll);
@@ -259,6 +262,8 @@ int route(int op, int64_t rows, int64_t H, rmsn_dtype_t wdt, int det, int form, 
         r.grid = g < cap ? g : cap;
         if (r.grid < 1) r.grid = 1;
         r.kind = RMSN_KIND_BWD_ROW_DET;
+        r.stream_loads = stream_level(rows, H, false);
+        if (k && k->stream_loads) r.stream_loads = k->stream_loads - 1;
         r.partial_f64 = rows > kPartialF32MaxRows ? 1 : 0;
         if (k && k->partial_f64) r.partial_f64 = k->partial_f64 == 1 ? 1 : 0;
         r.partials = r.grid;

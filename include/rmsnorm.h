@@ -221,7 +221,7 @@ typedef struct {
     int64_t grid;        /* blocks of the main kernel */
     int64_t partials;    /* dw partial rows written (0 if none) */
     int64_t reduce_grid; /* blocks of the dw reduce (column-task blocks for small T) */
-    int stream_loads;    /* RMSNorm row kernels' loads: 0 plain, 1 dy/dres non-temporal,
+    int stream_loads;    /* row kernels' loads: 0 plain, 1 dy/dres non-temporal,
                             2 all inputs non-temporal (a function of the shape) */
 } rmsn_route_t;
 

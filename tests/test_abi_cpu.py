@@ -276,24 +276,25 @@ def test_route_override_selects_atomic_and_rejects_bad_knobs():
 
 
 def test_route_stream_loads_policy_follows_shape():
-    """Non-temporal loads: 0 below 32M elements, 1 (dy/dres streamed) up to
-    a forward footprint of 256 MiB (the Infinity Cache), 2 above it; the
+    """Non-temporal loads: 0 below 32M elements, 1 (dy/dres streamed) below
+    a forward footprint of 256 MiB (the Infinity Cache), 2 from there on; the
     residual form counts four tensors in the forward, the plain form two."""
     MiE = 1024 * 1024
     for op in (0, 1):
         assert route(op, 4096, 4096)[1].stream_loads == 0          # 16M elements
         assert route(op, 32768 * 4, 256, 1)[1].stream_loads == 1   # 32M, 128 MiB forward
-        assert route(op, 32768 * 4, 256, 1, 1, 1)[1].stream_loads == 1  # residual: 256 MiB, not above
-        assert route(op, 40960 * 4, 256, 1)[1].stream_loads == 1
-        assert route(op, 40960 * 4, 256, 1, 1, 1)[1].stream_loads == 2  # residual: 320 MiB
+        assert route(op, 32768 * 4, 256, 1, 1, 1)[1].stream_loads == 2  # residual: 256 MiB
+        assert route(op, 32768 * 4 - 1, 256, 1, 1, 1)[1].stream_loads == 0  # just under both
         assert route(op, 131072, 2048, 1)[1].stream_loads == 2
         assert route(op, 32768 * 24, 256, 1)[1].stream_loads == 2
         assert route(op, 16384, 6144, 0, 1, 1)[1].stream_loads == 2
         # boundary: just under 32M elements stays plain
         assert route(op, 32 * MiE // 4096 - 1, 4096)[1].stream_loads == 0
-    # the column-task path and the LayerNorm routes do not use it
+    # the column-task path does not use it; LayerNorm counts x and y
     assert route(1, 64, 256, 1)[1].stream_loads == 0
-    assert route(2, 131072, 2048)[1].stream_loads == 0
+    assert route(2, 8192, 3584)[1].stream_loads == 0
+    assert route(3, 8192, 4096)[1].stream_loads == 1
+    assert route(2, 8192, 8192)[1].stream_loads == 2
     K = _lib.RouteKnobs
     try:
         k = K(); k.stream_loads = 3
