@@ -78,3 +78,38 @@ def test_dw_accuracy_sweep(family, T, H, wdt):
     if wdt == "f32":
         assert max(ours_max) <= max(eager_max), "worst dw error above the FP32 eager reference's"
     assert np.median(ours_med) <= np.median(eager_med), "median dw error above the FP32 eager median"
+
+
+# The pages' top windows: the token counts at which their earlier kernels
+# broke the dw budget (flashinfer PR "fix(cake_rmsnorm): sm_100a and sm_107a
+# dw-accuracy backward routes": H1536 at T 1048576 by 2.4x, H5120 from
+# T 262144, H512 above T 92912). This library keeps one FP64 accumulation
+# path at every T, so no cut is needed; these cases check that with the two
+# stress families, one seed each (the inputs are several GB).
+TOP_WINDOWS = [
+    (1048576, 1536, "f32", "same_sign"),
+    (1048576, 512, "bf16", "heavy_rows"),
+    (262144, 5120, "bf16", "same_sign"),
+]
+
+
+@pytest.mark.parametrize("T,H,wdt,family", TOP_WINDOWS)
+def test_dw_budget_top_windows(T, H, wdt, family):
+    print(f"top window T={T} H={H} w={wdt} family={family}", flush=True)
+    wl = synth.make(T=T, H=H, w_dtype=wdt, seed=7, **synth.FAMILIES[family])
+    r64, r32 = oracle_rstd32(wl.x, wl.w.f64, wl.eps)
+    _, _, dw64 = oracle.bwd(wl.dy, wl.x, r32.astype(np.float64), wl.w.f64, want_dx=False)
+    _, _, dw64_i = oracle.bwd(wl.dy, wl.x, r64, wl.w.f64, want_dx=False)
+    del r64
+    x, dy, w, rs = dev_bf16(wl.x), dev_bf16(wl.dy), dev_w(wl.w), dev_f32(r32)
+    del wl
+    worst = {}
+    for det in (True, False):
+        dx, dw = rn.rmsnorm_bwd(dy, x, rs, w, deterministic=det)
+        del dx
+        torch.cuda.synchronize()
+        dwn = dw.cpu().numpy().astype(np.float64)
+        worst[det] = max(float(np.max(np.abs(dwn - dw64) / (DW_ATOL + DW_RTOL * np.abs(dw64)))),
+                         float(np.max(np.abs(dwn - dw64_i) / (DW_ATOL + DW_RTOL * np.abs(dw64_i)))))
+    print(f"  worst dw err/budget det {worst[True]:.2e} non-det {worst[False]:.2e}", flush=True)
+    assert worst[True] <= 1.0 and worst[False] <= 1.0
