@@ -8,17 +8,19 @@ namespace rmsn {
 // slices: thread (chunk c, slice s) sums partial rows s, s + S, s + 2S, ...
 // in increasing order, four loads in flight at a time. The slice sums are
 // then added in a fixed order: a butterfly over the slices each wave holds,
-// then the waves in index order. Nothing depends on timing, so the result is
-// bit-reproducible. Columns below `split` go to out0, the others to out1
+// then the waves in index order (one thread per column). Nothing depends on
+// timing, so the result is bit-reproducible. Columns below `split` go to out0, the others to out1
 // (LayerNorm's dgamma and dbeta share one partial row); split is a multiple
 // of the chunk width.
 template <typename PT, int CC>
-__global__ void __launch_bounds__(1024) k_dw_reduce(const PT* __restrict__ part, int64_t P,
-                                                    int32_t H, float* __restrict__ dw,
-                                                    float* __restrict__ out1, int32_t split) {
+__global__ void __launch_bounds__(kReduceThreads) k_dw_reduce(const PT* __restrict__ part, int64_t P,
+                                                              int32_t H, float* __restrict__ dw,
+                                                              float* __restrict__ out1, int32_t split) {
     constexpr int CPC = 16 / sizeof(PT);  // columns per 16-byte chunk
-    __shared__ double sm_red[16][CC * CPC];
-    const int S = blockDim.x / CC;
+    constexpr int NCOL = CC * CPC;        // columns per block
+    constexpr int NW = kReduceThreads / 64;
+    constexpr int S = kReduceThreads / CC;
+    __shared__ double sm_red[NW][NCOL];
     const int cc = threadIdx.x % CC;
     const int s = threadIdx.x / CC;
     const int64_t col0 = ((int64_t)blockIdx.x * CC + cc) * CPC;
@@ -64,19 +66,22 @@ __global__ void __launch_bounds__(1024) k_dw_reduce(const PT* __restrict__ part,
         for (int m = CC; m < 64; m <<= 1) a[e] += __shfl_xor(a[e], m, 64);
     }
     const int wave = threadIdx.x >> 6;
-    const int nwaves = blockDim.x >> 6;
     if ((threadIdx.x & 63) < CC) {
 #pragma unroll
         for (int e = 0; e < CPC; ++e) sm_red[wave][cc * CPC + e] = a[e];
     }
     __syncthreads();
-    if (threadIdx.x < CC && col_ok) {
-        float* dst = col0 < split ? dw + col0 : out1 + (col0 - split);
-#pragma unroll
-        for (int e = 0; e < CPC; ++e) {
+    // chunks are whole columns of one side of split (H and split are
+    // multiples of 8 columns), so the per-column tests match the chunk's
+    if (threadIdx.x < NCOL) {
+        const int c = threadIdx.x;
+        const int64_t col = (int64_t)blockIdx.x * NCOL + c;
+        if (col < H) {
             double t = 0.0;
-            for (int w = 0; w < nwaves; ++w) t += sm_red[w][cc * CPC + e];
-            dst[e] = (float)t;
+#pragma unroll
+            for (int w = 0; w < NW; ++w) t += sm_red[w][c];
+            float* dst = col < split ? dw + col : out1 + (col - split);
+            *dst = (float)t;
         }
     }
 }
@@ -93,8 +98,8 @@ __global__ void __launch_bounds__(256) k_fill_zero(uint4* p, int64_t n16, uint8_
 
 int launch_col_reduce(const void* partial, const Route& rt, int32_t W, float* out0, float* out1,
                       int32_t split, hipStream_t s) {
-    const unsigned threads = (unsigned)rt.r.reduce_threads;
-    dim3 grid((unsigned)rt.r.reduce_grid), block(threads);
+    if (rt.r.reduce_threads != kReduceThreads) return RMSN_ERR_SHAPE;
+    dim3 grid((unsigned)rt.r.reduce_grid), block((unsigned)kReduceThreads);
     const size_t lds = 0;
     // the route sizes the grid for 16-byte chunks per block (kReduceChunks)
     if (rt.r.partial_f64)

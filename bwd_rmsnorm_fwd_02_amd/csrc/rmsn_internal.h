@@ -21,6 +21,9 @@ constexpr int kPartitionCUs = 256;
 // columns per block; 4 and 16 chunks measured slower at 4096 x 4096 and
 // 32768 x 4 x 256).
 constexpr int kReduceChunks = 8;
+// Threads per block of the dw reduce (16 waves: 128 slices of the partial
+// rows, one round of loads up to P = 512).
+constexpr int kReduceThreads = 1024;
 
 // Backward forms: plain rows, fused residual (h, optional dres), or plain
 // rows with rstd recomputed from x inside the backward.

@@ -269,7 +269,7 @@ int route(int op, int64_t rows, int64_t H, rmsn_dtype_t wdt, int det, int form, 
         r.partials = r.grid;
         const int psize = r.partial_f64 ? 8 : 4;
         r.reduce_grid = ceil_div(2 * H * psize, 16 * kReduceChunks);
-        r.reduce_threads = 1024;
+        r.reduce_threads = kReduceThreads;
         out->workspace = align256((size_t)r.partials * (size_t)(2 * H) * psize);
         (void)det;
         return RMSN_OK;
@@ -339,7 +339,7 @@ int route(int op, int64_t rows, int64_t H, rmsn_dtype_t wdt, int det, int form, 
         r.partials = r.grid;
         const int psize = r.partial_f64 ? 8 : 4;
         r.reduce_grid = ceil_div(H * psize, 16 * kReduceChunks);
-        r.reduce_threads = 1024;  // 128 slices: one round of loads up to P = 512
+        r.reduce_threads = kReduceThreads;
         out->workspace = align256((size_t)r.partials * (size_t)H * psize);
     } else {
         if (r.vec_per_lane != 1 || r.unroll > 2) return RMSN_ERR_SHAPE;  // compiled variants
