@@ -284,9 +284,10 @@ __device__ __forceinline__ void load_weights(const BwdParams& p, int slot, int l
 template <int NV, int U, typename WT, bool RES, bool WIDE, int MODE, bool RC = false, int NT = 0>
 __global__ void __launch_bounds__(WIDE ? (NV * U >= 4 ? 512 : 1024) : 256) k_bwd_row(BwdParams p) {
     // Rows above 8192 elements take four vectors per lane on 512 lanes (a
-    // 1024-lane group leaves 128 registers per lane); that shape has no room
-    // for a second tile and does not prefetch.
-    constexpr bool PF = U <= 2 && NV < 4;
+    // 1024-lane group leaves 128 registers per lane); with the row unpacked
+    // again after the exchange, the prefetched tile still fits (about 235
+    // registers).
+    constexpr bool PF = U <= 2;
     extern __shared__ double lds_bwd[];
     const int tid = threadIdx.x;
     const int slot = tid / p.tpr;

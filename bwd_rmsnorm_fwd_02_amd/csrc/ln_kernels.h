@@ -261,6 +261,12 @@ __device__ __forceinline__ void ln_bwd_ready(const LnBwdTile<NV, U>& t) {
     }
 }
 
+// Floats of the LDS row-sum exchange area of the backward: two sums per
+// wave of each row group, double-buffered (none for rows within one wave).
+__host__ __device__ inline int ln_bwd_exch_floats(int tpr, int rpb, int U, bool wide) {
+    return wide ? 2 * 2 * rpb * U * (tpr >> 6) : 0;
+}
+
 // Row-group sums of the two per-lane FP32 sums (sum g, sum g * xhat) of U
 // rows, one exchange for both.
 template <int U, bool WIDE>
@@ -310,28 +316,48 @@ __global__ void __launch_bounds__(WIDE ? (NV * U >= 4 ? 512 : 1024) : 256)
     // (a 1024-lane group would leave 128 registers per lane, too few for the
     // accumulators of both column sums); with those accumulators a second
     // tile does not fit either, so that shape does not prefetch.
-    constexpr bool PF = U <= 2 && NV < 4 && !(WIDE && NV == 2 && U == 1);
+    constexpr bool PF = U <= 2 && !(WIDE && NV == 2 && U == 1);
+    // With four vectors per lane the registers go to the FP64 dgamma sums
+    // and the two tiles: the FP32 dbeta sums live in LDS (each lane its own
+    // slots, same additions in the same order) and BF16 gamma stays packed,
+    // unpacked at each use.
+    constexpr bool BL = NV >= 4;
+    constexpr bool GPK = BL && sizeof(WT) == 2;
     extern __shared__ double lds_lnb[];
     const int tid = threadIdx.x;
     const int slot = tid / p.tpr;
     const int lr = tid - slot * p.tpr;
-    // LDS: [2H] doubles for the slot combine, then the row-sum exchange area
+    // LDS: [2H] doubles for the slot combine, then the row-sum exchange
+    // area, then (BL) the dbeta sums, [2 NV][blockDim] float4
     double* comb = lds_lnb;
     float* red = reinterpret_cast<float*>(lds_lnb + (p.rpb > 1 ? 2 * p.H : 0));
+    float4* abl = reinterpret_cast<float4*>(red + ln_bwd_exch_floats(p.tpr, p.rpb, U, WIDE));
 
-    float gv[NV][8];
+    float gv[GPK ? 1 : NV][8];
+    uint4 gq[GPK ? NV : 1];
     bool vok[NV];
 #pragma unroll
     for (int v = 0; v < NV; ++v) {
         const int vi = lr + v * p.tpr;
         vok[v] = (slot < p.rpb) && (vi < p.nvec);
-        if (vok[v]) {
+        if constexpr (GPK) {
+            gq[v] = vok[v] ? ld16(static_cast<const uint16_t*>(p.gamma) + (int64_t)vi * kVec)
+                           : make_uint4(0, 0, 0, 0);
+        } else if (vok[v]) {
             load_w8<WT>(p.gamma, vi, gv[v]);
         } else {
 #pragma unroll
             for (int e = 0; e < 8; ++e) gv[v][e] = 0.f;
         }
     }
+    auto gamma8 = [&](int v, float (&f)[8]) {
+        if constexpr (GPK) {
+            unpack8(opaque(gq[v]), f);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) f[e] = gv[v][e];
+        }
+    };
     double ag[NV][8];
     float ab[NV][8];
 #pragma unroll
@@ -341,6 +367,10 @@ __global__ void __launch_bounds__(WIDE ? (NV * U >= 4 ? 512 : 1024) : 256)
             ag[v][e] = 0.0;
             ab[v][e] = 0.f;
         }
+    if constexpr (BL) {
+#pragma unroll
+        for (int i = 0; i < 2 * NV; ++i) abl[i * blockDim.x + tid] = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
 
     const int64_t P = gridDim.x;
     const int64_t b = blockIdx.x;
@@ -363,13 +393,14 @@ __global__ void __launch_bounds__(WIDE ? (NV * U >= 4 ? 512 : 1024) : 256)
                 s2[k] = 0.f;
 #pragma unroll
                 for (int v = 0; v < NV; ++v) {
-                    float xf[8], dyf[8];
+                    float xf[8], dyf[8], gf[8];
                     unpack8(cur.x[k][v], xf);
                     unpack8(cur.dy[k][v], dyf);
+                    gamma8(v, gf);
                     float a = 0.f, c = 0.f;
 #pragma unroll
                     for (int e = 0; e < 8; ++e) {
-                        const float g = dyf[e] * gv[v][e];
+                        const float g = dyf[e] * gf[e];
                         const float xh = (xf[e] - cur.mu[k]) * cur.rs[k];
                         a += g;
                         c = __builtin_fmaf(g, xh, c);
@@ -392,7 +423,7 @@ __global__ void __launch_bounds__(WIDE ? (NV * U >= 4 ? 512 : 1024) : 256)
                 const double rs64 = (double)rs;
 #pragma unroll
                 for (int v = 0; v < NV; ++v) {
-                    float xf[8], dyf[8], o[8];
+                    float xf[8], dyf[8], o[8], gf[8];
                     // With two or more vectors per lane, holding the first
                     // loop's unpacked values across the exchange would crowd
                     // out the accumulators: recompute them (opaque copies).
@@ -403,15 +434,26 @@ __global__ void __launch_bounds__(WIDE ? (NV * U >= 4 ? 512 : 1024) : 256)
                         unpack8(cur.x[k][v], xf);
                         unpack8(cur.dy[k][v], dyf);
                     }
+                    gamma8(v, gf);
 #pragma unroll
                     for (int e = 0; e < 8; ++e) {
-                        const float g = dyf[e] * gv[v][e];
+                        const float g = dyf[e] * gf[e];
                         const float d = xf[e] - cur.mu[k];
                         const float xh = d * rs;
                         o[e] = (g - __builtin_fmaf(xh, c2, c1)) * rs;
                         if (live && vok[v]) {
                             ag[v][e] = __builtin_fma((double)(dyf[e] * d), rs64, ag[v][e]);
-                            ab[v][e] += dyf[e];
+                            if constexpr (!BL) ab[v][e] += dyf[e];
+                        }
+                    }
+                    if constexpr (BL) {
+                        if (live && vok[v]) {
+                            float4* q = abl + (2 * v) * blockDim.x + tid;
+                            float4 lo = q[0], hi = q[blockDim.x];
+                            lo.x += dyf[0]; lo.y += dyf[1]; lo.z += dyf[2]; lo.w += dyf[3];
+                            hi.x += dyf[4]; hi.y += dyf[5]; hi.z += dyf[6]; hi.w += dyf[7];
+                            q[0] = lo;
+                            q[blockDim.x] = hi;
                         }
                     }
                     out[k][v] = pack8(o);
@@ -434,6 +476,15 @@ __global__ void __launch_bounds__(WIDE ? (NV * U >= 4 ? 512 : 1024) : 256)
             if constexpr (!PF) {
                 if (r0 + stride < p.rows) ln_bwd_load<NV, U, NT>(p, r0 + stride, slot, lr, cur);
             }
+        }
+    }
+
+    if constexpr (BL) {
+#pragma unroll
+        for (int v = 0; v < NV; ++v) {
+            const float4 lo = abl[(2 * v) * blockDim.x + tid], hi = abl[(2 * v + 1) * blockDim.x + tid];
+            ab[v][0] = lo.x; ab[v][1] = lo.y; ab[v][2] = lo.z; ab[v][3] = lo.w;
+            ab[v][4] = hi.x; ab[v][5] = hi.y; ab[v][6] = hi.z; ab[v][7] = hi.w;
         }
     }
 
@@ -502,8 +553,9 @@ inline size_t ln_fwd_lds_bytes(const rmsn_route_t& r) {
 
 inline size_t ln_bwd_lds_bytes(const rmsn_route_t& r, int H) {
     size_t lds = r.rows_per_block > 1 ? sizeof(double) * 2 * (size_t)H : 0;
-    if (r.lanes_per_row > 64)
-        lds += sizeof(float) * 2 * 2 * (size_t)r.rows_per_block * r.unroll * (r.lanes_per_row / 64);
+    lds += sizeof(float) *
+           (size_t)ln_bwd_exch_floats(r.lanes_per_row, r.rows_per_block, r.unroll, r.lanes_per_row > 64);
+    if (r.vec_per_lane >= 4) lds += 16 * 2 * (size_t)r.vec_per_lane * r.block_threads;  // dbeta sums
     return lds;
 }
 
