@@ -39,16 +39,20 @@ constexpr double kMallBytes = 256.0 * 1024 * 1024;
 
 // Cache policy of the row kernels' loads (RMSNorm and LayerNorm), a
 // function of the shape only. When the forward's tensors (x and y, plus r
-// and h in the residual form) fill the Infinity Cache, nothing it read
-// survives to the backward, so every large input is loaded non-temporally
-// (2). Otherwise x
-// can still be found by the backward: from 32M elements only the tensors
-// read once (dy, dres) are streamed (1), which keeps them from evicting x;
-// below that (0) plain loads measured no faster. Step times against plain
-// loads everywhere, fwd + deterministic bwd in 200-step graphs: 131072 x
-// 2048 -1.3 %, 16384 x 6144 residual -6.0 %, 32768 x 24 x 256 strided
-// -6.9 %, 32768 x 4 x 256 -2.5 %, 262144 x 1536 -7.9 %, 65536 x 5120
-// -2.6 %, 4096 x 4096 unchanged.
+// and h in the residual form) fill the Infinity Cache, the backward loads
+// every large input non-temporally (2): it is their last reader in the step.
+// Otherwise x can still be found by the backward: from 32M elements only
+// the tensors read once (dy, dres) are streamed (1), which keeps them from
+// evicting x; below that (0) plain loads measured no faster. The forward
+// streams only inputs that no later kernel reads, x and r of the residual
+// form (whose backward reads h), and only at level 2: streaming the plain
+// form's x, which the backward reads again, made the step slower at every
+// size measured (up to 6 %). Step times, fwd + deterministic bwd in
+// 200-step graphs, against plain loads everywhere: 131072 x 2048 -2.7 %,
+// 16384 x 6144 residual -3.7 %, 32768 x 24 x 256 strided -11.3 %,
+// 32768 x 4 x 256 -2.1 %, 1048576 x 512 -6.4 %, 262144 x 1536 -8.2 %,
+// 65536 x 5120 -3.3 %, 8192 x 16384 -12.4 %, 4096 x 4096 unchanged;
+// LayerNorm 65536 x 4096 -10.3 %, 8192 x 16384 -1.8 %.
 int stream_level(int64_t rows, int64_t H, bool residual) {
     const double e = (double)rows * (double)H;
     const double fwd_bytes = e * 2.0 * (residual ? 4.0 : 2.0);
@@ -238,7 +242,7 @@ int route(int op, int64_t rows, int64_t H, rmsn_dtype_t wdt, int det, int form, 
         if (!((nv == 1 && u <= 2) || (nv == 2 && u <= 4 && u != 3) || (nv == 4 && u == 1)))
             return RMSN_ERR_SHAPE;
         r.kind = RMSN_KIND_FWD_ROW;
-        r.stream_loads = stream_level(rows, H, false);
+        r.stream_loads = 0;  // the backward reads x again
         if (g_have_knobs[2] && g_knobs[2].stream_loads) r.stream_loads = g_knobs[2].stream_loads - 1;
         const int bpc = sh.bpc > 0 ? sh.bpc : (2048 / r.block_threads > 0 ? 2048 / r.block_threads : 1);
         const int64_t cap = (int64_t)kPartitionCUs * bpc;
@@ -280,7 +284,7 @@ int route(int op, int64_t rows, int64_t H, rmsn_dtype_t wdt, int det, int form, 
         if (g_have_knobs[0]) apply_knobs(g_knobs[0], sh);
         if ((st = row_shape(0, nvec, sh, r)) != RMSN_OK) return st;
         r.kind = RMSN_KIND_FWD_ROW;
-        r.stream_loads = stream_level(rows, H, form == kFormResidual);
+        r.stream_loads = form == kFormResidual && stream_level(rows, H, true) == 2 ? 2 : 0;
         if (g_have_knobs[0] && g_knobs[0].stream_loads) r.stream_loads = g_knobs[0].stream_loads - 1;
         const int bpc = sh.bpc > 0 ? sh.bpc : (2048 / r.block_threads > 0 ? 2048 / r.block_threads : 1);
         const int64_t cap = (int64_t)kPartitionCUs * bpc;

@@ -221,8 +221,9 @@ typedef struct {
     int64_t grid;        /* blocks of the main kernel */
     int64_t partials;    /* dw partial rows written (0 if none) */
     int64_t reduce_grid; /* blocks of the dw reduce (column-task blocks for small T) */
-    int stream_loads;    /* row kernels' loads: 0 plain, 1 dy/dres non-temporal,
-                            2 all inputs non-temporal (a function of the shape) */
+    int stream_loads;    /* row kernels' non-temporal loads, a function of the shape:
+                            backward 1 dy/dres, 2 every input; forward 2 x and r
+                            (residual form only); 0 none */
 } rmsn_route_t;
 
 /* The route table: which kernel and launch shape serve this problem.

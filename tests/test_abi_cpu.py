@@ -276,33 +276,43 @@ def test_route_override_selects_atomic_and_rejects_bad_knobs():
 
 
 def test_route_stream_loads_policy_follows_shape():
-    """Non-temporal loads: 0 below 32M elements, 1 (dy/dres streamed) below
-    a forward footprint of 256 MiB (the Infinity Cache), 2 from there on; the
-    residual form counts four tensors in the forward, the plain form two."""
+    """Non-temporal loads in the backward: 0 below 32M elements, 1 (dy/dres
+    streamed) below a forward footprint of 256 MiB (the Infinity Cache), 2
+    from there on; the residual form counts four tensors in the forward, the
+    plain form two. The forward streams only the residual form's x and r, at
+    level 2; LayerNorm's forward never (its backward reads x again)."""
     MiE = 1024 * 1024
-    for op in (0, 1):
-        assert route(op, 4096, 4096)[1].stream_loads == 0          # 16M elements
-        assert route(op, 32768 * 4, 256, 1)[1].stream_loads == 1   # 32M, 128 MiB forward
-        assert route(op, 32768 * 4, 256, 1, 1, 1)[1].stream_loads == 2  # residual: 256 MiB
-        assert route(op, 32768 * 4 - 1, 256, 1, 1, 1)[1].stream_loads == 0  # just under both
-        assert route(op, 131072, 2048, 1)[1].stream_loads == 2
-        assert route(op, 32768 * 24, 256, 1)[1].stream_loads == 2
-        assert route(op, 16384, 6144, 0, 1, 1)[1].stream_loads == 2
-        # boundary: just under 32M elements stays plain
-        assert route(op, 32 * MiE // 4096 - 1, 4096)[1].stream_loads == 0
-    # the column-task path does not use it; LayerNorm counts x and y
+    b = lambda *a: route(1, *a)[1].stream_loads
+    f = lambda *a: route(0, *a)[1].stream_loads
+    assert b(4096, 4096) == 0                       # 16M elements
+    assert b(32768 * 4, 256, 1) == 1                # 32M, 128 MiB forward
+    assert b(32768 * 4, 256, 1, 1, 1) == 2          # residual: 256 MiB
+    assert b(32768 * 4 - 1, 256, 1, 1, 1) == 0      # just under both
+    assert b(131072, 2048, 1) == 2
+    assert b(32768 * 24, 256, 1) == 2
+    assert b(16384, 6144, 0, 1, 1) == 2
+    assert b(32 * MiE // 4096 - 1, 4096) == 0
+    for shape in [(4096, 4096), (32768 * 4, 256, 1), (131072, 2048, 1), (32768 * 24, 256, 1)]:
+        assert f(*shape) == 0                       # plain forward: x is read again
+    assert f(16384, 6144, 0, 1, 1) == 2             # residual forward, 768 MiB
+    assert f(32768 * 4, 256, 1, 1, 1) == 2
+    assert f(32768 * 2, 256, 1, 1, 1) == 0          # residual, 128 MiB
+    # the column-task path does not use it; LayerNorm: backward as RMSNorm's
     assert route(1, 64, 256, 1)[1].stream_loads == 0
-    assert route(2, 8192, 3584)[1].stream_loads == 0
+    assert route(2, 8192, 8192)[1].stream_loads == 0
+    assert route(3, 8192, 3584)[1].stream_loads == 0
     assert route(3, 8192, 4096)[1].stream_loads == 1
-    assert route(2, 8192, 8192)[1].stream_loads == 2
+    assert route(3, 8192, 8192)[1].stream_loads == 2
     K = _lib.RouteKnobs
     try:
         k = K(); k.stream_loads = 3
         assert lib.rmsnorm_route_override(1, ctypes.byref(k)) == 0
         assert route(1, 4096, 4096)[1].stream_loads == 2
-        k.stream_loads = 1
         assert lib.rmsnorm_route_override(0, ctypes.byref(k)) == 0
-        assert route(0, 131072, 2048)[1].stream_loads == 0
+        assert route(0, 131072, 2048)[1].stream_loads == 2
+        k.stream_loads = 1
+        assert lib.rmsnorm_route_override(1, ctypes.byref(k)) == 0
+        assert route(1, 131072, 2048, 1)[1].stream_loads == 0
         k.stream_loads = 4
         assert lib.rmsnorm_route_override(1, ctypes.byref(k)) == -3
     finally:
