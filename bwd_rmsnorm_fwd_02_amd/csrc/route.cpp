@@ -111,6 +111,24 @@ constexpr Entry kBwdTable[] = {
     {1 << 30, 4, 1, 0, 1},  // H <= 16384: 512 lanes, four vectors each
 };
 
+// Recompute-form backward (rmsnorm_bwd_recompute), timed as forward +
+// recompute backward in step graphs at the workloads of each width class
+// (T 4096 to 1048576). Its rows end in a serial chain (FP64 sum of squares,
+// exchange, square root and division) that the plain backward does not
+// have, so it wants more rows in flight per CU: more vectors per lane,
+// smaller blocks, more of them.
+constexpr Entry kRcBwdTable[] = {
+    {32, 2, 1, 128, 4},     // H <= 256: as the plain backward
+    {64, 4, 1, 64, 4},      // H <= 512: 16 lanes per row, 4 rows per block
+    {192, 2, 2, 128, 4},    // H <= 1536: 128 lanes, 2 rows per iteration, 4 blocks per CU
+    {256, 2, 2, 256, 2},    // H <= 2048: 2 row groups of 128 lanes, 2 blocks per CU
+    {512, 2, 2, 256, 2},    // H <= 4096: 256 lanes, 2 rows per iteration
+    {640, 4, 1, 384, 1},    // H <= 5120: 2 row groups of 192 lanes
+    {768, 4, 1, 0, 2},      // H <= 6144: 192 lanes, one row per block, 2 blocks per CU
+    {1024, 4, 1, 0, 2},     // H <= 8192: 256 lanes, one row per block, 2 blocks per CU
+    {1 << 30, 4, 1, 0, 1},  // H <= 16384: as the plain backward
+};
+
 template <size_t N>
 Shape lookup(const Entry (&t)[N], int nvec) {
     for (const Entry& e : t) {
@@ -157,6 +175,7 @@ constexpr Entry kLnBwdTable[] = {
 
 Shape default_fwd(int nvec) { return lookup(kFwdTable, nvec); }
 Shape default_bwd(int nvec) { return lookup(kBwdTable, nvec); }
+Shape default_rc_bwd(int nvec) { return lookup(kRcBwdTable, nvec); }
 Shape default_ln_fwd(int nvec) { return lookup(kLnFwdTable, nvec); }
 Shape default_ln_bwd(int nvec) { return lookup(kLnBwdTable, nvec); }
 
@@ -318,7 +337,7 @@ int route(int op, int64_t rows, int64_t H, rmsn_dtype_t wdt, int det, int form, 
     }
 
     // Large T: row kernel with register dw sums per block.
-    Shape sh = default_bwd(nvec);
+    Shape sh = form == kFormRecompute ? default_rc_bwd(nvec) : default_bwd(nvec);
     const rmsn_route_knobs_t* k = g_have_knobs[1] ? &g_knobs[1] : nullptr;
     if (k) apply_knobs(*k, sh);
     if ((st = row_shape(1, nvec, sh, r)) != RMSN_OK) return st;

@@ -171,8 +171,7 @@ def test_route_recompute_form_runs_the_row_kernel_at_every_t():
             assert st == 0 and r.kind == _lib.RMSN_KIND_BWD_ROW_DET
             _, plain = route(1, rows, 256, 1, det, 0)
             if rows > 64:
-                # above the column-task window both forms share one launch shape
-                # and partition, so their dx and dw bits agree for equal rstd
+                # at H 256 the recompute table takes the plain backward's shape
                 for f in ("grid", "vec_per_lane", "lanes_per_row", "rows_per_block", "unroll",
                           "partials", "partial_f64"):
                     assert getattr(r, f) == getattr(plain, f), f
@@ -181,6 +180,24 @@ def test_route_recompute_form_runs_the_row_kernel_at_every_t():
     assert r.partials >= 1
     assert lib.rmsnorm_bwd_workspace_bytes(64, 256, 1, 1) >= r.partials * 256 * 4
     assert route(1, 100, 256, 0, 1, 3)[0] == -3  # no such form
+
+
+def test_route_recompute_form_has_its_own_launch_shapes():
+    """The recompute backward's table: (NV, U, lanes per row, rows per
+    block, grid) per width class, as timed in step graphs."""
+    want = {(131072, 2048): (2, 2, 128, 2, 512), (4096, 4096): (2, 2, 256, 1, 512),
+            (65536, 5120): (4, 1, 192, 2, 256), (1048576, 512): (4, 1, 16, 4, 1024),
+            (262144, 1536): (2, 2, 128, 1, 1024), (16384, 6144): (4, 1, 192, 1, 512),
+            (8192, 8192): (4, 1, 256, 1, 512), (8192, 16384): (4, 1, 512, 1, 256),
+            (786432, 256): (2, 1, 16, 8, 1024)}
+    for (rows, H), shape in want.items():
+        st, r = route(1, rows, H, 0, 1, 2)
+        assert st == 0
+        assert (r.vec_per_lane, r.unroll, r.lanes_per_row, r.rows_per_block, r.grid) == shape, (rows, H)
+        assert r.vec_per_lane * r.lanes_per_row * 8 >= H
+        # the workspace query covers the recompute form's partials
+        need = lib.rmsnorm_bwd_workspace_bytes(rows, H, 0, 1)
+        assert need >= r.partials * H * (8 if r.partial_f64 else 4)
 
 
 def test_route_deterministic_partition_is_a_function_of_shape():

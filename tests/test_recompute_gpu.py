@@ -14,14 +14,19 @@ Checks:
   from the oracle's by up to one FP32 ulp: d(dx)/d(rstd) = g - 3 xhat c, so
   |delta dx| <= 2^-23 rstd (|g| + 3 |xhat c|).
 * bit for bit against the plain backward fed the GPU forward's rstd, where
-  both run the row kernel (rows > 64): same launch shape and partition, and
+  both run the row kernel (rows > 64) and the plain backward is forced
+  (route override) onto the recompute route's launch shape and partition:
   the recomputed rstd equals the forward's (the FP64 sum of the FP32 group
-  sums is exact for these inputs).
+  sums is exact for these inputs). The two routes' default shapes differ
+  (the recompute form has its own table), and with them the summation
+  order of the row dot products and of dw.
 * the checkpointed step as one HIP graph, replayed several times with eager
   work in between: every replay reproduces the eager result bit for bit, and
   the recompute forward reproduces the first forward's y and rstd.
 """
 from __future__ import annotations
+
+import contextlib
 
 import numpy as np
 import pytest
@@ -34,6 +39,28 @@ from tests.parity import check_dw, check_dx, dx_bound, oracle_rstd32, to_f64
 from tests.test_parity_gpu import DEV, _announce, dev_bf16, dev_f32, dev_w, host_bits
 
 pytestmark = pytest.mark.gpu
+
+
+# CUs the row kernels' fixed partition is sized for (grid = min(tiles, 256 x
+# blocks per CU))
+PARTITION_CUS = 256
+
+
+@contextlib.contextmanager
+def recompute_shape(rows, H, w_dtype):
+    """Run the plain backward at the launch shape the recompute form routes
+    to, so that both sum in the same order."""
+    r = rn.rmsnorm_route_query("bwd", rows, H, w_dtype, recompute=True)
+    rn.rmsnorm_route_override("bwd", vec_per_lane=r["vec_per_lane"], unroll=r["unroll"],
+                              rows_per_block=r["rows_per_block"],
+                              blocks_per_cu=-(-r["grid"] // PARTITION_CUS))
+    try:
+        p = rn.rmsnorm_route_query("bwd", rows, H, w_dtype)
+        assert (p["vec_per_lane"], p["unroll"], p["rows_per_block"], p["grid"]) == \
+            (r["vec_per_lane"], r["unroll"], r["rows_per_block"], r["grid"])
+        yield
+    finally:
+        rn.rmsnorm_route_override("bwd")
 
 
 def _rc_bound(wl, r32, c64):
@@ -78,8 +105,9 @@ def test_bwd_recompute_small(T, H, wdt):
         assert np.array_equal(host_bits(dx2), outs[True][0])
     if T > 64:
         _, rstd = rn.rmsnorm_fwd(x, w, wl.eps)
-        dxp, dwp = rn.rmsnorm_bwd(dy, x, rstd, w, deterministic=True)
-        torch.cuda.synchronize()
+        with recompute_shape(T, H, w.dtype):
+            dxp, dwp = rn.rmsnorm_bwd(dy, x, rstd, w, deterministic=True)
+            torch.cuda.synchronize()
         assert np.array_equal(host_bits(dxp), outs[True][0]), "dx differs from the plain backward"
         assert np.array_equal(dwp.cpu().numpy().view(np.uint32), outs[True][1].view(np.uint32)), \
             "dw differs from the plain backward"
@@ -109,8 +137,9 @@ def test_bwd_recompute_strided_heads(T, heads, H, row):
     check_dw("dw", dw.cpu().numpy(), dw64)
     if T * heads > 64:
         _, rstd = rn.rmsnorm_fwd_strided(xview, w, wl.eps)
-        dxp, dwp = rn.rmsnorm_bwd_strided(dy, xview, rstd, w, deterministic=True)
-        torch.cuda.synchronize()
+        with recompute_shape(T * heads, H, w.dtype):
+            dxp, dwp = rn.rmsnorm_bwd_strided(dy, xview, rstd, w, deterministic=True)
+            torch.cuda.synchronize()
         assert np.array_equal(host_bits(dxp).reshape(-1, H), dx_rc)
         assert torch.equal(dwp.view(torch.int32), dw.view(torch.int32))
 
@@ -122,10 +151,28 @@ FULL = ["c2_T4096_H4096_bf16w", "c3_T131072_H2048_f32w_heavy",
 @pytest.mark.parametrize("name", FULL)
 def test_bwd_recompute_full_size(name):
     """At the full workload sizes: bit-identical to the plain backward fed
-    the GPU forward's rstd (every row and column), and dw against the oracle."""
+    the GPU forward's rstd at the same launch shape (every row and column),
+    and dw against the oracle."""
     _announce(f"bwd_recompute full {name}")
     wl = synth.config(name, seed=0)
     w = dev_w(wl.w)
+    with recompute_shape(wl.rows, wl.H, w.dtype):
+        x, dy, dxp, dwp = _plain_full(wl, w)
+    for det in (True, False):
+        dx, dw = rn.rmsnorm_bwd_recompute(dy, x, w, wl.eps, deterministic=det)
+        torch.cuda.synchronize()
+        assert torch.equal(dx.view(torch.int16), dxp.view(torch.int16)), f"dx det={det}"
+        assert torch.equal(dw.view(torch.int32), dwp.view(torch.int32)), f"dw det={det}"
+    r64, r32 = oracle_rstd32(wl.x, wl.w.f64, wl.eps)
+    _, _, dw64 = oracle.bwd(wl.dy, wl.x, r32.astype(np.float64), wl.w.f64, want_dx=False)
+    _, _, dw64_i = oracle.bwd(wl.dy, wl.x, r64, wl.w.f64, want_dx=False)
+    worst = check_dw("dw (forward's rstd)", dw.cpu().numpy(), dw64)
+    worst_i = check_dw("dw (FP64 rstd)", dw.cpu().numpy(), dw64_i)
+    print(f"{name}: recompute dw worst {worst:.2e} / {worst_i:.2e} of budget", flush=True)
+
+
+def _plain_full(wl, w):
+    """GPU forward, then the plain deterministic backward fed its rstd."""
     if wl.xbuf is not None:
         T, heads, H = wl.T, wl.heads, wl.H
         xbuf = dev_bf16(wl.xbuf)
@@ -144,17 +191,8 @@ def test_bwd_recompute_full_size(name):
         else:
             _, rstd = rn.rmsnorm_fwd(x, w, wl.eps)
             dxp, dwp = rn.rmsnorm_bwd(dy, x, rstd, w, deterministic=True)
-    for det in (True, False):
-        dx, dw = rn.rmsnorm_bwd_recompute(dy, x, w, wl.eps, deterministic=det)
-        torch.cuda.synchronize()
-        assert torch.equal(dx.view(torch.int16), dxp.view(torch.int16)), f"dx det={det}"
-        assert torch.equal(dw.view(torch.int32), dwp.view(torch.int32)), f"dw det={det}"
-    r64, r32 = oracle_rstd32(wl.x, wl.w.f64, wl.eps)
-    _, _, dw64 = oracle.bwd(wl.dy, wl.x, r32.astype(np.float64), wl.w.f64, want_dx=False)
-    _, _, dw64_i = oracle.bwd(wl.dy, wl.x, r64, wl.w.f64, want_dx=False)
-    worst = check_dw("dw (forward's rstd)", dw.cpu().numpy(), dw64)
-    worst_i = check_dw("dw (FP64 rstd)", dw.cpu().numpy(), dw64_i)
-    print(f"{name}: recompute dw worst {worst:.2e} / {worst_i:.2e} of budget", flush=True)
+    torch.cuda.synchronize()
+    return x, dy, dxp, dwp
 
 
 @pytest.mark.parametrize("recompute_in_bwd", [False, True])
