@@ -101,12 +101,12 @@ constexpr Entry kFwdTable[] = {
 };
 constexpr Entry kBwdTable[] = {
     {32, 2, 1, 128, 4},     // H <= 256: 16 lanes per row, 8 rows per block, 4 blocks per CU
-    {64, 2, 1, 128, 4},     // H <= 512: 32 lanes per row, 4 rows per block, 4 blocks per CU
+    {64, 2, 2, 256, 1},     // H <= 512: 32 lanes per row, 8 row groups, 2 rows per iteration
     {192, 1, 1, 768, 1},    // H <= 1536: one lane per vector, 768-thread blocks
-    {256, 1, 2, 512, 1},    // H <= 2048: 2 row groups of up to 256 lanes, 1 block per CU
+    {256, 1, 1, 1024, 1},   // H <= 2048: 4 row groups of 256 lanes, 1 block per CU
     {512, 1, 1, 0, 2},      // H <= 4096: one row per block, 2 blocks per CU
-    {640, 1, 1, 0, 1},      // H <= 5120: one lane per vector, one row per block
-    {768, 2, 2, 0, 1},      // H <= 6144
+    {640, 4, 1, 384, 1},    // H <= 5120: 2 row groups of 192 lanes, four vectors each
+    {768, 1, 1, 0, 1},      // H <= 6144: 768 lanes, one row per block
     {1024, 1, 1, 0, 1},     // H <= 8192: 1024 lanes, one row per block
     {1 << 30, 4, 1, 0, 1},  // H <= 16384: 512 lanes, four vectors each
 };
