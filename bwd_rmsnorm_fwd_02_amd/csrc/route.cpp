@@ -91,11 +91,11 @@ struct Entry {
 constexpr Entry kFwdTable[] = {
     {32, 4, 1, 256, 2},     // H <= 256: 8 lanes per row, 32 rows per block
     {64, 4, 1, 256, 2},     // H <= 512: 16 lanes per row, 16 rows per block
-    {192, 2, 1, 1024, 1},   // H <= 1536: up to 128 lanes per row, 1024-thread blocks
-    {256, 2, 1, 512, 1},    // H <= 2048
+    {192, 4, 2, 256, 1},    // H <= 1536: 64 lanes per row, 4 row groups, 2 rows per iteration
+    {256, 2, 1, 512, 4},    // H <= 2048: 4 row groups of 128 lanes, 4 blocks per CU
     {512, 2, 4, 256, 4},    // H <= 4096: 256 lanes per row, 4 rows per iteration
-    {640, 2, 1, 0, 2},      // H <= 5120: one row per block, 2 blocks per CU
-    {768, 2, 1, 0, 1},      // H <= 6144
+    {640, 2, 1, 640, 2},    // H <= 5120: 2 row groups of 320 lanes, 2 blocks per CU
+    {768, 2, 1, 768, 1},    // H <= 6144: 2 row groups of 384 lanes
     {1024, 2, 1, 0, 2},     // H <= 8192
     {1 << 30, 4, 1, 0, 1},  // H <= 16384
 };
