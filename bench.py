@@ -235,7 +235,7 @@ def cpu_baseline(args, rows, step_bytes, op, oracle_rows):
                               "sample": f"{reps_1} repetition(s) in {el_1:.1f} s"}}
 
 
-def result_line(args, metric, op, value, t, step_bytes, config, traffic, cpu):
+def result_line(args, metric, op, value, t, step_bytes, config, traffic, cpu, route=None):
     K = t["K"]
     walls, walls_nd, median = t["walls"], t["walls_nd"], t["median"]
     return {
@@ -269,6 +269,7 @@ def result_line(args, metric, op, value, t, step_bytes, config, traffic, cpu):
                      "frac": round(t["achieved"] / HBM_PEAK_GBPS, 4),
                      "traffic": traffic, "algorithmic_bytes": t["dom_bytes"]},
         "cpu_baseline": cpu,
+        "route": route,
     }
 
 
@@ -356,8 +357,11 @@ def bench_layernorm(args, np, torch, rn, _lib, lib, synth, dev, d16) -> int:
         rec = json.load(open(tr_path))
         if rec.get("source_hash") == _b.source_hash() and t["dom_name"] in rec.get("kernels", {}):
             traffic = rec["kernels"][t["dom_name"]]["bytes_per_launch"]
+    wt = torch.bfloat16 if wl.gamma.dtype == "bf16" else torch.float32
+    route = {"fwd": rn.rmsnorm_route_query("ln_fwd", T, H, wt),
+             "bwd": rn.rmsnorm_route_query("ln_bwd", T, H, wt)}
     out = result_line(args, f"LayerNorm {op} effective HBM GB/s, per (T,H)", op, t["value"], t,
-                      step_bytes, config, traffic, cpu)
+                      step_bytes, config, traffic, cpu, route)
     print(json.dumps(out), flush=True)
     return 0
 
@@ -551,7 +555,12 @@ def main() -> int:
               "global_batch": rows, "seq_len": T, "parallelism": "none (1 GPU)",
               "buffer_sets": n_sets}
     metric = METRIC if op == "fwd+bwd" else f"RMSNorm {op} effective HBM GB/s, per (T,H)"
-    out = result_line(args, metric, op, value, t, step_bytes, config, traffic, cpu)
+    # the launch shapes, partition and load policy the route chose (host-side query)
+    wt = torch.bfloat16 if wl.w.dtype == "bf16" else torch.float32
+    route = {"fwd": rn.rmsnorm_route_query("fwd", rows, H, wt, residual=residual),
+             "bwd": rn.rmsnorm_route_query("bwd", rows, H, wt, residual=residual,
+                                           recompute=(op == "fwd+bwd_recompute"))}
+    out = result_line(args, metric, op, value, t, step_bytes, config, traffic, cpu, route)
     print(json.dumps(out), flush=True)
     return 0
 
