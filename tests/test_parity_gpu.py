@@ -56,6 +56,9 @@ SMALL = [
     (300, 2048, "f32"), (129, 6144, "bf16"), (70, 1032, "bf16"), (257, 16384, "bf16"),
     (1000, 512, "f32"), (2049, 1536, "bf16"), (5, 16384, "f32"), (40, 6144, "f32"),
     (9000, 128, "bf16"), (700, 5120, "f32"),
+    # ragged for the multi-row launch shapes (4 rows per iteration at H 2048,
+    # 2 row groups at H 5120), FP64 partials above 8192 rows
+    (303, 2048, "bf16"), (701, 5120, "bf16"), (10007, 2048, "f32"),
 ]
 
 
