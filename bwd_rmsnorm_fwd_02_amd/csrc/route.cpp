@@ -79,8 +79,10 @@ size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
 
 // Default launch shapes of the row kernels by width (nvec 16-byte vectors
 // per row), chosen by timing every compiled shape on MI355X in step mode
-// (forward then backward, as training runs them) at H 256 (per-head views),
-// 512, 1536, 2048, 4096, 5120, 6144 (residual) and 8192.
+// (forward then backward in graphs, as training runs them, with the load
+// policy above) at the workloads of each width: H 256 (per-head views), 512,
+// 1536, 2048, 4096, 5120, 6144 (plain and residual), 8192 and 16384, then
+// confirming each change with an in-process A/B.
 // rpb_threads sets the row groups per block (threads / lanes per row).
 struct Shape {
     int nv, unroll, rpb, bpc;
