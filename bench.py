@@ -453,7 +453,9 @@ def main() -> int:
     sets = []
     for i in range(n_sets):
         s = dict(x=x0.clone(), dy=dy0.clone(), y=torch.empty(rows, H, dtype=torch.bfloat16, device=dev),
-                 dx=torch.empty_like(x0) if wl.xbuf is not None else torch.empty(rows, H, dtype=torch.bfloat16, device=dev),
+                 # the strided form's gap columns are never written: zero them so
+                 # the replay check (which zeroes outputs first) sees the same gap
+                 dx=torch.zeros_like(x0) if wl.xbuf is not None else torch.empty(rows, H, dtype=torch.bfloat16, device=dev),
                  rstd=torch.empty(rows, dtype=torch.float32, device=dev),
                  dw=torch.empty(H, dtype=torch.float32, device=dev))
         if residual:
