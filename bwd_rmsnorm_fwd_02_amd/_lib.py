@@ -11,6 +11,8 @@ import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libbwd_rmsnorm.so")
+# Written by the build: the code hash of the sources the library was built from.
+HASH_PATH = os.path.join(HERE, "libbwd_rmsnorm.hash")
 
 RMSN_BF16 = 0
 RMSN_F32 = 1
@@ -86,6 +88,17 @@ def load() -> ctypes.CDLL:
         raise RuntimeError(
             f"{LIB_PATH} is missing: build it with `python -m bwd_rmsnorm_fwd_02_amd.build` "
             "(there is no fallback path)")
+    if os.path.exists(HASH_PATH):
+        # A library built from other sources may disagree with the structs
+        # below (a larger route record written past a smaller one corrupts
+        # the interpreter's memory), so refuse it.
+        from . import build
+        with open(HASH_PATH) as fh:
+            built = fh.read().strip()
+        if built != build.source_hash():
+            raise RuntimeError(
+                f"{LIB_PATH} was built from other sources (code hash {built}, sources "
+                f"{build.source_hash()}): rebuild it with `python -m bwd_rmsnorm_fwd_02_amd.build`")
     lib = ctypes.CDLL(LIB_PATH)
     p, i64, i32, f32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float
     sz = ctypes.c_size_t

@@ -29,15 +29,50 @@ COMMON = [
 ]
 
 
+def _code_only(src: str) -> str:
+    """C/C++ source with comments removed and whitespace runs collapsed, so
+    that the hash follows the code and not its comments."""
+    out = []
+    i, n, quote = 0, len(src), None
+    while i < n:
+        c = src[i]
+        if quote:
+            out.append(c)
+            if c == "\\" and i + 1 < n:
+                out.append(src[i + 1])
+                i += 2
+                continue
+            if c == quote:
+                quote = None
+            i += 1
+        elif c in "\"'":
+            quote = c
+            out.append(c)
+            i += 1
+        elif src.startswith("//", i):
+            j = src.find("\n", i)
+            i = n if j < 0 else j
+        elif src.startswith("/*", i):
+            j = src.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def source_hash() -> str:
-    """Hash of every source and header that goes into the library."""
+    """Hash of the code (comments and layout ignored) of every source and
+    header that goes into the library. Measurement records (the HBM traffic
+    files under profiles/) carry it, and are used only while it matches."""
     h = hashlib.sha256()
     files = sorted(os.listdir(CSRC))
     for f in files:
-        with open(os.path.join(CSRC, f), "rb") as fh:
-            h.update(f.encode() + b"\0" + fh.read())
-    with open(os.path.join(os.path.dirname(HERE), "include", "rmsnorm.h"), "rb") as fh:
-        h.update(fh.read())
+        with open(os.path.join(CSRC, f), encoding="utf-8") as fh:
+            h.update(f.encode() + b"\0" + _code_only(fh.read()).encode())
+    with open(os.path.join(os.path.dirname(HERE), "include", "rmsnorm.h"), encoding="utf-8") as fh:
+        h.update(_code_only(fh.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -335,3 +335,25 @@ def test_route_stream_loads_policy_follows_shape():
     finally:
         lib.rmsnorm_route_override(0, None)
         lib.rmsnorm_route_override(1, None)
+
+
+def test_loader_refuses_a_library_built_from_other_sources(tmp_path, monkeypatch):
+    """The binding's structs must match the library's: a build whose recorded
+    code hash differs from the sources is refused before it is loaded."""
+    stale = tmp_path / "libbwd_rmsnorm.hash"
+    stale.write_text("0000000000000000\n")
+    monkeypatch.setattr(_lib, "HASH_PATH", str(stale))
+    monkeypatch.setattr(_lib, "_lib", None)
+    with pytest.raises(RuntimeError, match="built from other sources"):
+        _lib.load()
+
+
+def test_code_hash_ignores_comments_and_layout():
+    from bwd_rmsnorm_fwd_02_amd import build
+    a = "int f(int x) { // note\n  return x + 1; /* more */ }\n"
+    b = "int f(int x) {\n\n    return x + 1;   }"
+    c = "int f(int x) { return x + 2; }"
+    s = 'const char* s = "// kept";'
+    assert build._code_only(a) == build._code_only(b)
+    assert build._code_only(a) != build._code_only(c)
+    assert "// kept" in build._code_only(s)
