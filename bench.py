@@ -249,7 +249,10 @@ def result_line(args, metric, op, value, t, step_bytes, config, traffic, cpu, ro
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        # the arithmetic: FP32 row math with FP64 sums (rstd, dw); BF16 and the
+        # weight dtype are storage only
+        "dtype": "f32",
+        "io_dtype": "bf16 activations and gradients, weight as configured",
         "data": "synthetic",
         "config": config,
         "replay_ms_per_step": {"median": round(t["ms_per_step"], 5), "min": round(walls[0] / K, 5),
