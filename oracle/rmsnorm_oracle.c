@@ -41,10 +41,15 @@ typedef struct {
 
 static void nsum_add(nsum_t* a, double v) {
     double t = a->s + v;
-    if (fabs(a->s) >= fabs(v)) {
-        a->c += (a->s - t) + v;
-    } else {
-        a->c += (v - t) + a->s;
+    /* The correction term is defined for finite sums only: once the sum is
+     * infinite or NaN it is the plain sum's value (inf - inf in the
+     * correction would turn an infinite sum into NaN). */
+    if (isfinite(t)) {
+        if (fabs(a->s) >= fabs(v)) {
+            a->c += (a->s - t) + v;
+        } else {
+            a->c += (v - t) + a->s;
+        }
     }
     a->s = t;
 }

@@ -315,3 +315,31 @@ def test_residual_add_matches_float32_sum_and_torch_rounding():
     for i in range(2000, 2200):
         exact = float(synth.bits_to_f32(x[i:i + 1])[0]) + float(synth.bits_to_f32(r[i:i + 1])[0])
         assert int(h[i]) == _exact_round_bf16(exact)
+
+
+def test_non_finite_inputs_propagate_as_ieee_arithmetic_fixes():
+    """Non-finite inputs are not special-cased: a row holding +inf has an
+    infinite sum of squares, so rstd = 1/sqrt(inf) = 0 exactly, xhat = inf * 0
+    is NaN at that element and 0 elsewhere; its c is NaN, so its dx is NaN
+    throughout, and dw is NaN only in that column. A NaN in dy spoils its
+    row's dx and its own column of dw; a NaN in x spoils its row (rstd, y,
+    dx) and every column of dw."""
+    H, T = 16, 4
+    w = 1.0 + 0.1 * np.arange(H)
+    x = synth.bf16_bits(np.linspace(-2, 2, T * H, dtype=np.float32).reshape(T, H))
+    dy = synth.bf16_bits(np.linspace(1, -1, T * H, dtype=np.float32).reshape(T, H))
+    x[1, 3] = 0x7F80   # +inf
+    dy[2, 7] = 0x7FC0  # NaN
+    rstd, y = oracle.fwd(x, w, EPS)
+    assert rstd[1] == 0.0 and np.isfinite(rstd[[0, 2, 3]]).all()
+    assert np.isnan(y[1, 3]) and np.all(y[1, np.arange(H) != 3] == 0.0)
+    assert np.isfinite(y[[0, 2, 3]]).all()
+    dx, _, dw = oracle.bwd(dy, x, rstd, w)
+    assert np.isnan(dx[1]).all() and np.isnan(dx[2]).all()
+    assert np.isfinite(dx[[0, 3]]).all()
+    assert set(np.flatnonzero(np.isnan(dw))) == {3, 7}
+    x[0, 5] = 0x7FC0   # NaN in x
+    rstd, y = oracle.fwd(x, w, EPS)
+    assert np.isnan(rstd[0]) and np.isnan(y[0]).all()
+    _, _, dw = oracle.bwd(dy, x, rstd, w)
+    assert np.isnan(dw).all()
