@@ -380,3 +380,51 @@ def test_route_variants(T, H, wdt, op, knobs):
             assert np.array_equal(outs[0][0], dx_det)
     finally:
         rn.rmsnorm_route_override(op)
+
+
+# ------------------------------------------------------ non-finite inputs
+
+@pytest.mark.parametrize("nan_in_x", [False, True])
+@pytest.mark.parametrize("wdt", ["bf16", "f32"])
+@pytest.mark.parametrize("T", [48, 300])
+def test_non_finite_inputs_propagate_like_the_oracle(T, wdt, nan_in_x):
+    """Nothing special-cases non-finite inputs: +inf in x, NaN in dy (and
+    NaN in x) leave NaN exactly where the FP64 oracle has NaN in y, rstd, dx
+    and dw (row 9 with +inf gets rstd 0), and every other element stays
+    within the usual budgets. T 48 takes the column-task kernel, T 300 the
+    row kernel."""
+    H = 1024
+    _announce(f"non-finite T={T} H={H} w={wdt} nan_in_x={nan_in_x}")
+    wl = synth.make(T=T, H=H, w_dtype=wdt, seed=11 + T)
+    x, dy = wl.x.copy(), wl.dy.copy()
+    x[9, 3] = 0x7F80       # +inf
+    dy[20, 100] = 0x7FC0   # NaN
+    if nan_in_x:
+        x[5, 17] = 0x7FC0
+    r64, y64 = oracle.fwd(x, wl.w.f64, wl.eps)
+    r32 = oracle.round_f32(r64)
+    dx64, c64, dw64 = oracle.bwd(dy, x, r32.astype(np.float64), wl.w.f64)
+    w = dev_w(wl.w)
+    y, rstd = rn.rmsnorm_fwd(dev_bf16(x), w, wl.eps)
+    dx, dw = rn.rmsnorm_bwd(dev_bf16(dy), dev_bf16(x), dev_f32(r32), w, deterministic=True)
+    dx_nd, dw_nd = rn.rmsnorm_bwd(dev_bf16(dy), dev_bf16(x), dev_f32(r32), w, deterministic=False)
+    torch.cuda.synchronize()
+    yb, rs, dxb, dwn = host_bits(y), rstd.cpu().numpy(), host_bits(dx), dw.cpu().numpy()
+    assert np.array_equal(np.isnan(to_f64(yb)), np.isnan(y64)), "y NaN pattern"
+    assert np.array_equal(np.isnan(rs), np.isnan(r64)), "rstd NaN pattern"
+    assert rs[9] == 0.0 and r64[9] == 0.0
+    assert np.array_equal(np.isnan(to_f64(dxb)), np.isnan(dx64)), "dx NaN pattern"
+    assert np.array_equal(np.isnan(dwn), np.isnan(dw64)), "dw NaN pattern"
+    assert np.array_equal(host_bits(dx_nd), dxb), "dx differs between modes"
+    assert np.array_equal(np.isnan(dw_nd.cpu().numpy()), np.isnan(dw64)), "non-det dw NaN pattern"
+    fy = ~np.isnan(y64)
+    check_bf16_strict("y (finite)", yb[fy], y64[fy])
+    fr = np.isfinite(r64) & (r64 != 0.0)
+    check_rstd("rstd (finite)", rs[fr], r64[fr])
+    rows = np.isfinite(dx64).all(axis=1)
+    E = dx_bound(to_f64(x[rows]), to_f64(dy[rows]), wl.w.f64, r32.astype(np.float64)[rows],
+                 c64[rows], H)
+    check_dx("dx (finite rows)", dxb[rows], dx64[rows], E)
+    fc = ~np.isnan(dw64)
+    check_dw("dw (finite columns)", dwn[fc], dw64[fc])
+    assert nan_in_x == bool(np.isnan(dw64).all())
