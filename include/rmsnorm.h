@@ -56,7 +56,16 @@
 extern "C" {
 #endif
 
-typedef enum { RMSN_BF16 = 0, RMSN_F32 = 1 } rmsn_dtype_t;
+/* Weight dtype. The two outer enumerators are never valid; they make every
+ * int value a value of this type, so that a caller may pass any int (a C
+ * caller, or a binding) and get RMSN_ERR_DTYPE back for unsupported ones
+ * rather than undefined behaviour in the C++ implementation. */
+typedef enum {
+    RMSN_DTYPE_INVALID_ = -1,
+    RMSN_BF16 = 0,
+    RMSN_F32 = 1,
+    RMSN_DTYPE_MAX_ = 0x7fffffff
+} rmsn_dtype_t;
 
 enum {
     RMSN_OK = 0,
