@@ -251,8 +251,9 @@ int rmsnorm_route_query(int op, int64_t rows, int64_t H, rmsn_dtype_t w_dtype,
  * the next call of that op fail with RMSN_ERR_SHAPE instead of launching.
  * Overriding the backward changes the deterministic partition, hence the dw
  * bits (they stay reproducible for a fixed setting). The small-T column-task
- * route is not affected. op as for rmsnorm_route_query. Process-wide; NULL
- * clears. */
+ * route is not affected. op as for rmsnorm_route_query. Process-wide, and
+ * not synchronised: set it while no other host thread is calling the
+ * library. NULL clears. */
 typedef struct {
     int vec_per_lane;   /* 1, 2 or 4 (backward 4 only with unroll 1) */
     int unroll;         /* 1, 2 or 4; only 1 when a row spans several waves */
