@@ -106,7 +106,7 @@ constexpr Entry kBwdTable[] = {
     {64, 2, 2, 256, 1},     // H <= 512: 32 lanes per row, 8 row groups, 2 rows per iteration
     {192, 1, 1, 768, 1},    // H <= 1536: one lane per vector, 768-thread blocks
     {256, 1, 1, 1024, 1},   // H <= 2048: 4 row groups of 256 lanes, 1 block per CU
-    {512, 1, 1, 0, 2},      // H <= 4096: one row per block, 2 blocks per CU
+    {512, 1, 1, 1024, 1},   // H <= 4096: 2 row groups of 512 lanes (3 of 320 up to 2560), 1 block per CU
     {640, 4, 1, 384, 1},    // H <= 5120: 2 row groups of 192 lanes, four vectors each
     {768, 1, 1, 0, 1},      // H <= 6144: 768 lanes, one row per block
     {1024, 1, 1, 0, 1},     // H <= 8192: 1024 lanes, one row per block

@@ -94,7 +94,7 @@ int main() {
     // backward
     EXPECT(rmsnorm_bwd(DY, X, rs, W, RMSN_BF16, 1, DX, dw, T, H, WS, need, s), RMSN_ERR_LAUNCH);
     EXPECT(rmsnorm_bwd(DY, X, rs, W, RMSN_BF16, 0, DX, dw, T, H, WS, need, s), RMSN_ERR_LAUNCH);
-    EXPECT(rmsnorm_bwd(DY, X, rs, W, RMSN_BF16, 1, DX, dw, T, H, WS, need - 1, s), RMSN_ERR_WORKSPACE);
+    EXPECT(rmsnorm_bwd(DY, X, rs, W, RMSN_BF16, 1, DX, dw, T, H, WS, 4096, s), RMSN_ERR_WORKSPACE);
     EXPECT(rmsnorm_bwd(DY, X, rs, W, RMSN_BF16, 1, DY, dw, T, H, WS, need, s), RMSN_ERR_ALIAS);
     EXPECT(rmsnorm_bwd(DY, X, rs, W, RMSN_BF16, 1, DX, nullptr, T, H, WS, need, s), RMSN_ERR_NULL);
     EXPECT(rmsnorm_bwd(DY, X, rs, W, RMSN_BF16, 1, DX, dw, 64, 256, nullptr, 0, s), RMSN_ERR_LAUNCH);

@@ -107,7 +107,13 @@ def test_bwd_argument_errors():
     DY, X, RS, W, DX, DW, WS = (A + i * 0x4000000 for i in range(7))
     need = lib.rmsnorm_bwd_workspace_bytes(T, H, 0, 1)
     assert need > 0
-    assert f(_fake(DY), _fake(X), _fake(RS), _fake(W), 0, 1, _fake(DX), _fake(DW), T, H, _fake(WS), need - 1, s) == -5
+    # the query covers every backward form; the plain route's own partial
+    # rows need this much
+    st, r = route(1, T, H, 0, 1, 0)
+    assert st == 0 and r.partials > 0
+    plain = -(-r.partials * H * (8 if r.partial_f64 else 4) // 256) * 256
+    assert need >= plain
+    assert f(_fake(DY), _fake(X), _fake(RS), _fake(W), 0, 1, _fake(DX), _fake(DW), T, H, _fake(WS), plain - 1, s) == -5
     assert f(_fake(DY), _fake(X), _fake(RS), _fake(W), 0, 1, _fake(DX), _fake(DW), T, H, None, need, s) == -5
     assert f(_fake(DY), _fake(X), _fake(RS), _fake(W), 0, 1, _fake(DX), _fake(DW), T, H, _fake(WS + 8), need, s) == -5
     assert f(_fake(DY), _fake(X), _fake(RS), _fake(W), 0, 1, _fake(DX), None, T, H, _fake(WS), need, s) == -1
