@@ -78,6 +78,8 @@ def test_dw_accuracy_sweep(family, T, H, wdt):
         eager_med.append(float(np.median(ee)))
         eager_max.append(float(np.max(ee)))
         worst_eager = max(worst_eager, float(np.max(ee / tol)))
+        if len(SEEDS) > 5 and (seed + 1) % 20 == 0:
+            print(f"  {family} T={T} H={H}: {seed + 1}/{len(SEEDS)} inputs", flush=True)
     print(f"family={family} T={T} H={H} w={wdt} inputs={len(SEEDS)}: worst dw err/budget "
           f"det {worst[True]:.2e} non-det {worst[False]:.2e}; FP32 eager {worst_eager:.2e}; "
           f"median err ours {np.median(ours_med):.2e} eager {np.median(eager_med):.2e}", flush=True)
