@@ -299,22 +299,25 @@ def test_route_override_selects_atomic_and_rejects_bad_knobs():
 
 
 def test_route_stream_loads_policy_follows_shape():
-    """Non-temporal loads in the backward: 0 below 32M elements, 1 (dy/dres
-    streamed) below a forward footprint of 256 MiB (the Infinity Cache), 2
-    from there on; the residual form counts four tensors in the forward, the
-    plain form two. The forward streams only the residual form's x and r, at
+    """Non-temporal loads in the RMSNorm backward: 1 (dy/dres streamed)
+    below a forward footprint of 256 MiB (the Infinity Cache), 2 (every
+    input) from there on; the residual form counts four tensors in the
+    forward, the plain form two. LayerNorm's backward streams nothing below
+    32M elements. The forward streams only the residual form's x and r, at
     level 2; LayerNorm's forward never (its backward reads x again)."""
     MiE = 1024 * 1024
     b = lambda *a: route(1, *a)[1].stream_loads
     f = lambda *a: route(0, *a)[1].stream_loads
-    assert b(4096, 4096) == 0                       # 16M elements
+    assert b(4096, 4096) == 1                       # 16M elements
+    assert b(65, 256) == 1
     assert b(32768 * 4, 256, 1) == 1                # 32M, 128 MiB forward
     assert b(32768 * 4, 256, 1, 1, 1) == 2          # residual: 256 MiB
-    assert b(32768 * 4 - 1, 256, 1, 1, 1) == 0      # just under both
+    assert b(32768 * 4 - 1, 256, 1, 1, 1) == 1      # just under
     assert b(131072, 2048, 1) == 2
     assert b(32768 * 24, 256, 1) == 2
     assert b(16384, 6144, 0, 1, 1) == 2
-    assert b(32 * MiE // 4096 - 1, 4096) == 0
+    assert b(32 * MiE // 4096 - 1, 4096) == 1
+    assert route(1, 4096, 4096, 0, 1, 2)[1].stream_loads == 1   # recompute form
     for shape in [(4096, 4096), (32768 * 4, 256, 1), (131072, 2048, 1), (32768 * 24, 256, 1)]:
         assert f(*shape) == 0                       # plain forward: x is read again
     assert f(16384, 6144, 0, 1, 1) == 2             # residual forward, 768 MiB
