@@ -59,6 +59,9 @@ SMALL = [
     # ragged for the multi-row launch shapes (4 rows per iteration at H 2048,
     # 2 row groups at H 5120), FP64 partials above 8192 rows
     (303, 2048, "bf16"), (701, 5120, "bf16"), (10007, 2048, "f32"),
+    # widths between 2048 and 4096: three row groups of 320 lanes per block
+    # up to H 2560, two of 384 or 448 lanes above
+    (333, 2304, "bf16"), (1001, 2560, "f32"), (97, 3072, "bf16"), (129, 3584, "f32"),
 ]
 
 
