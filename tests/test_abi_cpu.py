@@ -206,6 +206,31 @@ def test_route_recompute_form_has_its_own_launch_shapes():
         assert need >= r.partials * H * (8 if r.partial_f64 else 4)
 
 
+def test_route_plain_backward_launch_shapes():
+    """The tuned backward table at each workload: (NV, U, lanes per row,
+    row groups per block, grid, FP64 partials, load policy), as timed in
+    step graphs on MI355X."""
+    want = {
+        (4096, 4096, 0, 0): (1, 1, 512, 2, 256, 0, 1),
+        (131072, 2048, 1, 0): (1, 1, 256, 4, 256, 1, 2),
+        (16384, 6144, 0, 1): (1, 1, 768, 1, 256, 1, 2),
+        (786432, 256, 1, 0): (2, 1, 16, 8, 1024, 1, 2),
+        (131072, 256, 1, 0): (2, 1, 16, 8, 1024, 1, 1),
+        (1048576, 512, 0, 0): (2, 2, 32, 8, 256, 1, 2),
+        (262144, 1536, 1, 0): (1, 1, 192, 4, 256, 1, 2),
+        (65536, 5120, 0, 0): (4, 1, 192, 2, 256, 1, 2),
+        (8192, 16384, 0, 0): (4, 1, 512, 1, 256, 0, 2),
+        (8192, 8192, 0, 0): (1, 1, 1024, 1, 256, 0, 2),
+    }
+    for (rows, H, wdt, res), shape in want.items():
+        st, r = route(1, rows, H, wdt, 1, res)
+        assert st == 0
+        got = (r.vec_per_lane, r.unroll, r.lanes_per_row, r.rows_per_block, r.grid, r.partial_f64,
+               r.stream_loads)
+        assert got == shape, (rows, H, got)
+        assert r.partials == r.grid and r.block_threads == r.lanes_per_row * r.rows_per_block
+
+
 def test_route_deterministic_partition_is_a_function_of_shape():
     # same answer for both weight dtypes and for the residual form
     for rows, H in [(4096, 4096), (131072, 2048), (16384, 6144), (786432, 256), (131072, 256)]:
