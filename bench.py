@@ -2,12 +2,13 @@
 """RMSNorm-for-training throughput on one MI355X: fwd + bwd effective HBM GB/s.
 
 A step is one pass of the whole path over one batch: the forward
-(x -> y, rstd) and the deterministic backward (dy, x, rstd -> dx, dw) of the
-RMSNorm workload x[T=4096, H=4096] BF16 with a BF16 weight (the workload the
-metric is quoted on; pass --config for the others). Inputs are seeded
-synthetic tensors already resident in HBM. Consecutive steps rotate over
-enough buffer sets (>= 1 GiB in the cycle) that no step finds its tensors in
-the 256 MB Infinity Cache, so the figure is an HBM figure.
+(x -> y, rstd) and the deterministic backward (dy, x, rstd -> dx, dw). The
+headline workload is the largest of the pages' five, x[T=131072, H=2048] BF16
+with an FP32 weight and 1 % of the rows scaled by 8 (pass --config for the
+others). Inputs are seeded synthetic tensors already resident in HBM.
+Consecutive steps rotate over enough buffer sets (>= 1 GiB in the cycle) that
+no step finds its tensors in the 256 MB Infinity Cache, so the figure is an
+HBM figure.
 
 --norm layernorm times LayerNorm instead (the other normalisation of the
 benchmark_normalization table on the TE page; its workloads are named
@@ -25,14 +26,25 @@ checkpointed step: forward, forward recompute, backward):
                        x itself (plain forms): the checkpointed step with the
                        recompute forward folded into the backward
 
-Timing:
-* value: K steps captured in one HIP graph (the pages time graph replays),
-  replayed --replays times, each between two synchronisations; the median
-  replay gives ms_per_step; GB/s of algorithmic bytes.
-* roofline: the same K steps launched eagerly with the library's per-kernel
-  HIP-event timers on the launch stream; the dominant kernel is the
-  backward row kernel (the forward for --op fwd); achieved = its
-  algorithmic bytes per launch / its mean event-timed duration; peak 8 TB/s.
+Timing (the pages' protocol, Cake page "Measurement", on HIP graphs):
+* a replay is one HIP graph holding K = --steps steps; its GPU span is
+  timed with two events on the replay stream. Each graph is replayed
+  --replays times (201), split over --rounds (3) interleaved rounds in which
+  the graphs take turns in a rotating order: the deterministic graph, an
+  A/A second capture of the same step, and the non-deterministic graph;
+* ms_per_step is the median replay span over K, with p10 and p90 beside it;
+  aa_noise = |1 - median(A) / median(A')|, the noise floor of the figure;
+  value = algorithmic bytes of one step / ms_per_step;
+* before each round, one untimed replay of each deterministic graph is
+  checked bit for bit against the eager result;
+* roofline: the same K steps launched eagerly, each library kernel bracketed
+  by HIP events recorded on its launch stream by the dispatch itself; the
+  dominant kernel is the backward row kernel (the forward for --op fwd);
+  achieved = its algorithmic bytes per launch / its mean duration; peak
+  8 TB/s. frac_cold is the same kernel timed in backward-only steps (no
+  forward before it, so nothing of x is left in the caches);
+* per_config: fwd, bwd and fwd+bwd of every workload of the family, with the
+  same protocol, in the same run (--no-per-config skips it);
 * cpu_baseline: the FP64 oracle on the same work, called on row slices from
   a pool of host threads (the oracle's C code runs without the interpreter
   lock), and single-threaded beside it.
@@ -56,13 +68,17 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
 METRIC = "RMSNorm fwd+bwd effective HBM GB/s and % of 8 TB/s peak, per (T,H)"
-DEFAULT_CONFIG = "c2_T4096_H4096_bf16w"
+DEFAULT_CONFIG = "c3_T131072_H2048_f32w_heavy"
 DEFAULT_LN_CONFIG = "ln_T8192_H4096_bf16w"
 OPS = ("fwd+bwd", "fwd", "bwd", "2xfwd+bwd", "fwd+bwd_recompute")
+P = ctypes.c_void_p
 
 
 def algorithmic_bytes(rows: int, H: int, sw: int, residual: bool, with_dres: bool):
-    """Bytes the path must move (per launch): see the design doc, measurement."""
+    """Bytes the path must move per launch: (forward, backward row kernel,
+    whole backward). Forward: read x (and r), write y (and h), write rstd,
+    read w. Backward: read dy, x (h), (dres), rstd, w; write dx; the reduce
+    writes dw."""
     e = rows * H
     fwd = (8 if residual else 4) * e + 4 * rows + H * sw
     bwd_row = ((8 if with_dres else 6) if residual else 6) * e + 4 * rows + H * sw
@@ -80,24 +96,211 @@ def ln_algorithmic_bytes(rows: int, H: int, sw: int):
     return fwd, bwd_row, bwd_row + 8 * H
 
 
-def time_steps(args, torch, rn, _lib, dev, sets, fwd, step, n_fwd, has_bwd, bwd_keys,
-               step_bytes, fwd_b, bwd_row_b, bwd_b):
-    """Graph-replay and per-kernel timing of K steps (shared by both norms)."""
-    import ctypes as _ct
-    P = _ct.c_void_p
+def gbps(nbytes: float, ms: float) -> float:
+    return nbytes / (ms * 1e-3) / 1e9
+
+
+def pct(v, q):
+    s = sorted(v)
+    if not s:
+        return None
+    k = (len(s) - 1) * q
+    lo = math.floor(k)
+    hi = min(lo + 1, len(s) - 1)
+    return s[lo] + (s[hi] - s[lo]) * (k - lo)
+
+
+# ------------------------------------------------------------- workloads
+
+class Work:
+    """Device buffers of one workload and the library calls of its ops."""
+
+    def __init__(self, **kw):
+        self.__dict__.update(kw)
+
+    def n_fwd(self, op):
+        return {"fwd+bwd": 1, "fwd": 1, "bwd": 0, "2xfwd+bwd": 2, "fwd+bwd_recompute": 1}[op]
+
+    def step_bytes(self, op):
+        fwd_b, _, bwd_b = self.bytes
+        if op == "fwd+bwd_recompute":
+            bwd_b -= 4 * self.rows  # the recompute backward reads no rstd
+        return self.n_fwd(op) * fwd_b + (bwd_b if op != "fwd" else 0)
+
+    def step_fn(self, op):
+        n_fwd, has_bwd = self.n_fwd(op), op != "fwd"
+        rc = op == "fwd+bwd_recompute"
+
+        def step(s, det, stream):
+            for _ in range(n_fwd):
+                self.fwd(s, stream)
+            if has_bwd:
+                self.bwd(s, det, stream, rc)
+        return step
+
+
+def n_sets_for(per_set_bytes: int) -> int:
+    return int(min(16, max(2, math.ceil((1 << 30) / per_set_bytes))))
+
+
+def prepare_rmsnorm(name, seed, torch, np, synth, _lib, lib, dev):
+    wl = synth.config(name, seed=seed)
+    rows, H, T, heads = wl.rows, wl.H, wl.T, wl.heads
+    residual = wl.r is not None
+    with_dres = wl.dres is not None
+    sw = 2 if wl.w.dtype == "bf16" else 4
+    wdt = _lib.RMSN_BF16 if sw == 2 else _lib.RMSN_F32
+
+    def d16(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    w = d16(wl.w.bits) if wl.w.dtype == "bf16" else torch.from_numpy(wl.w.f32.copy()).to(dev)
+    x0 = d16(wl.xbuf if wl.xbuf is not None else wl.x)
+    dy0 = d16(wl.dy)
+    r0 = d16(wl.r) if residual else None
+    dres0 = d16(wl.dres) if with_dres else None
+    per_set = x0.numel() * 2 + dy0.numel() * 2 + 2 * rows * H * 2 * (2 if residual else 1)
+    n_sets = n_sets_for(per_set)
+    sets = []
+    for _ in range(n_sets):
+        s = dict(x=x0.clone(), dy=dy0.clone(), y=torch.empty(rows, H, dtype=torch.bfloat16, device=dev),
+                 # the strided form's gap columns are never written: zero them so
+                 # the replay check (which zeroes outputs first) sees the same gap
+                 dx=(torch.zeros_like(x0) if wl.xbuf is not None
+                     else torch.empty(rows, H, dtype=torch.bfloat16, device=dev)),
+                 rstd=torch.empty(rows, dtype=torch.float32, device=dev),
+                 dw=torch.empty(H, dtype=torch.float32, device=dev))
+        if residual:
+            s["r"] = r0.clone()
+            s["h"] = torch.empty(rows, H, dtype=torch.bfloat16, device=dev)
+            s["dres"] = dres0.clone() if with_dres else None
+        sets.append(s)
+    del x0, dy0, r0, dres0
+    # one workspace per mode, so the two graphs never share one
+    ws = {}
+    for det in (0, 1):
+        nb = max(lib.rmsnorm_bwd_workspace_bytes(rows, H, wdt, det), 256)
+        raw = torch.empty(nb + 256, dtype=torch.uint8, device=dev)
+        ws[det] = (raw, P(raw.data_ptr() + (-raw.data_ptr()) % 256), nb)
+    if wl.xbuf is not None:
+        xv = _lib.View(T, heads, H, wl.x_stride_t, wl.x_stride_h)
+    else:
+        xv = _lib.View(T, heads, H, heads * H, H)
+    cv = _lib.View(T, heads, H, heads * H, H)
+    dxv = xv if wl.xbuf is not None else cv
+    eps = ctypes.c_float(wl.eps)
+
+    def fwd(s, stream):
+        if residual:
+            _lib.check(lib.rmsnorm_residual_fwd(P(s["x"].data_ptr()), P(s["r"].data_ptr()),
+                                                P(w.data_ptr()), wdt, eps, P(s["h"].data_ptr()),
+                                                P(s["y"].data_ptr()), P(s["rstd"].data_ptr()),
+                                                rows, H, stream))
+        else:
+            _lib.check(lib.rmsnorm_fwd_strided(P(s["x"].data_ptr()), xv, P(w.data_ptr()), wdt, eps,
+                                               P(s["y"].data_ptr()), cv, P(s["rstd"].data_ptr()),
+                                               stream))
+
+    def bwd(s, det, stream, rc=False):
+        _, wsp, nb = ws[det]
+        if residual:
+            _lib.check(lib.rmsnorm_residual_bwd(P(s["dy"].data_ptr()), P(s["h"].data_ptr()),
+                                                P(s["dres"].data_ptr()) if with_dres else None,
+                                                P(s["rstd"].data_ptr()), P(w.data_ptr()), wdt, det,
+                                                P(s["dx"].data_ptr()), P(s["dw"].data_ptr()), rows, H,
+                                                wsp, nb, stream))
+        elif rc:
+            _lib.check(lib.rmsnorm_bwd_recompute(P(s["dy"].data_ptr()), cv, P(s["x"].data_ptr()), xv,
+                                                 P(w.data_ptr()), wdt, eps, det,
+                                                 P(s["dx"].data_ptr()), dxv, P(s["dw"].data_ptr()),
+                                                 wsp, nb, stream))
+        else:
+            _lib.check(lib.rmsnorm_bwd_strided(P(s["dy"].data_ptr()), cv, P(s["x"].data_ptr()), xv,
+                                               P(s["rstd"].data_ptr()), P(w.data_ptr()), wdt, det,
+                                               P(s["dx"].data_ptr()), dxv, P(s["dw"].data_ptr()),
+                                               wsp, nb, stream))
+
+    return Work(name=name, norm="rmsnorm", wl=wl, rows=rows, T=T, heads=heads, H=H,
+                residual=residual, with_dres=with_dres, wdtype=wl.w.dtype, sets=sets, ws=ws,
+                fwd=fwd, bwd=bwd, out_keys=("y", "dx", "dw"),
+                bytes=algorithmic_bytes(rows, H, sw, residual, with_dres))
+
+
+def prepare_layernorm(name, seed, torch, np, synth, _lib, lib, dev):
+    wl = synth.ln_config(name, seed=seed)
+    T, H = wl.T, wl.H
+    sw = 2 if wl.gamma.dtype == "bf16" else 4
+    wdt = _lib.RMSN_BF16 if sw == 2 else _lib.RMSN_F32
+
+    def d16(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    def wdev(wt):
+        return d16(wt.bits) if wt.dtype == "bf16" else torch.from_numpy(wt.f32.copy()).to(dev)
+
+    gam, bet = wdev(wl.gamma), wdev(wl.beta)
+    x0, dy0 = d16(wl.x), d16(wl.dy)
+    n_sets = n_sets_for(4 * T * H * 2)
+    sets = []
+    for _ in range(n_sets):
+        sets.append(dict(x=x0.clone(), dy=dy0.clone(), y=torch.empty_like(x0), dx=torch.empty_like(x0),
+                         mean=torch.empty(T, dtype=torch.float32, device=dev),
+                         rstd=torch.empty(T, dtype=torch.float32, device=dev),
+                         dg=torch.empty(H, dtype=torch.float32, device=dev),
+                         db=torch.empty(H, dtype=torch.float32, device=dev)))
+    del x0, dy0
+    ws = {}
+    for det in (0, 1):
+        nb = max(lib.layernorm_bwd_workspace_bytes(T, H, wdt, det), 256)
+        raw = torch.empty(nb + 256, dtype=torch.uint8, device=dev)
+        ws[det] = (raw, P(raw.data_ptr() + (-raw.data_ptr()) % 256), nb)
+    eps = ctypes.c_float(wl.eps)
+
+    def fwd(s, stream):
+        _lib.check(lib.layernorm_fwd(P(s["x"].data_ptr()), P(gam.data_ptr()), P(bet.data_ptr()), wdt,
+                                     eps, P(s["y"].data_ptr()), P(s["mean"].data_ptr()),
+                                     P(s["rstd"].data_ptr()), T, H, stream))
+
+    def bwd(s, det, stream, rc=False):
+        _, wsp, nb = ws[det]
+        _lib.check(lib.layernorm_bwd(P(s["dy"].data_ptr()), P(s["x"].data_ptr()),
+                                     P(s["mean"].data_ptr()), P(s["rstd"].data_ptr()),
+                                     P(gam.data_ptr()), wdt, det, P(s["dx"].data_ptr()),
+                                     P(s["dg"].data_ptr()), P(s["db"].data_ptr()), T, H, wsp, nb,
+                                     stream))
+
+    return Work(name=name, norm="layernorm", wl=wl, rows=T, T=T, heads=1, H=H, residual=False,
+                with_dres=False, wdtype=wl.gamma.dtype, sets=sets, ws=ws, fwd=fwd, bwd=bwd,
+                out_keys=("y", "dx", "dg", "db"), bytes=ln_algorithmic_bytes(T, H, sw))
+
+
+# --------------------------------------------------------------- timing
+
+def same_bits(torch, a, b):
+    va = a.view(torch.int16) if a.dtype == torch.bfloat16 else a.view(torch.int32)
+    vb = b.view(torch.int16) if b.dtype == torch.bfloat16 else b.view(torch.int32)
+    return torch.equal(va, vb)
+
+
+def measure_op(args, torch, rn, _lib, dev, wk, op, nondet=True):
+    """Graph-replay timing of K steps of `op` under the replay protocol, and
+    per-kernel event timing of the same K steps launched eagerly."""
+    sets = wk.sets
     n_sets = len(sets)
     K, W = args.steps, args.warmup
     cur = torch.cuda.current_stream(dev)
     sp = P(cur.cuda_stream)
+    step = wk.step_fn(op)
+    has_bwd = op != "fwd"
+    out_keys = [k for k in wk.out_keys if (k == "y" and wk.n_fwd(op)) or (k != "y" and has_bwd)]
 
     # every set gets a forward's rstd (and h) first, so a backward-only step
     # has its inputs; then the eager warm-up and a reference result for set 0
     for s in sets:
-        fwd(s, sp)
+        wk.fwd(s, sp)
     for i in range(W):
         step(sets[i % n_sets], 1, sp)
     torch.cuda.synchronize()
-    out_keys = (["y"] if n_fwd else []) + (list(bwd_keys) if has_bwd else [])
     ref = {k: sets[0][k].clone() for k in out_keys}
 
     def capture(det: int):
@@ -112,51 +315,45 @@ def time_steps(args, torch, rn, _lib, dev, sets, fwd, step, n_fwd, has_bwd, bwd_
         torch.cuda.synchronize()
         return g
 
-    def same_bits(a, b):
-        return torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a.view(torch.int32),
-                           b.view(torch.int16) if b.dtype == torch.bfloat16 else b.view(torch.int32))
+    graphs = [("det", capture(1)), ("det_aa", capture(1))]
+    if nondet and has_bwd:
+        graphs.append(("nondet", capture(0)))
 
-    def timed_replays(g, check: bool):
-        """Median wall and GPU ms of --replays replays; every replay of the
-        deterministic graph must reproduce the eager result bit for bit."""
-        g.replay()  # warm
+    def check(g, tag):
+        for k in out_keys:
+            sets[0][k].zero_()
         torch.cuda.synchronize()
-        walls, gpus = [], []
-        for _ in range(max(1, args.replays)):
-            for k in out_keys:
-                sets[0][k].zero_()
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        g.replay()
+        torch.cuda.synchronize()
+        for k in out_keys:
+            assert same_bits(torch, sets[0][k], ref[k]), f"{wk.name} {op} {tag}: graph {k} != eager"
+
+    rounds = max(1, args.rounds)
+    per_round = max(1, math.ceil(args.replays / rounds))
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(per_round)]
+    spans = {k: [] for k, _ in graphs}
+    for rnd in range(rounds):
+        order = graphs[rnd % len(graphs):] + graphs[:rnd % len(graphs)]
+        for key, g in order:
+            if key != "nondet":
+                check(g, key)
+            else:
+                g.replay()  # untimed, as the deterministic graphs' checked replay
+            for i in range(per_round):
+                ev[i][0].record(cur)
+                g.replay()
+                ev[i][1].record(cur)
             torch.cuda.synchronize()
-            t0 = time.perf_counter()
-            e0.record()
-            g.replay()
-            e1.record()
-            torch.cuda.synchronize()
-            walls.append((time.perf_counter() - t0) * 1e3)
-            gpus.append(e0.elapsed_time(e1))
-            if check:
-                for k in out_keys:
-                    assert same_bits(sets[0][k], ref[k]), f"graph {k} != eager"
-        walls.sort()
-        gpus.sort()
-        return walls, gpus
+            spans[key] += [ev[i][0].elapsed_time(ev[i][1]) for i in range(per_round)]
+    del graphs
 
-    g_det = capture(1)
-    walls, gpus = timed_replays(g_det, check=True)
-    del g_det
-    walls_nd = None
-    if has_bwd:
-        g_nd = capture(0)
-        walls_nd, _ = timed_replays(g_nd, check=False)
-        del g_nd
+    def stats(v):
+        return {"median": pct(v, 0.5) / K, "p10": pct(v, 0.1) / K, "p90": pct(v, 0.9) / K,
+                "replays": len(v)}
 
-    def median(v):
-        n = len(v)
-        return v[n // 2] if n % 2 else 0.5 * (v[n // 2 - 1] + v[n // 2])
-
-    wall_ms, gpu_ms = median(walls), median(gpus)
-    ms_per_step = wall_ms / K
-    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+    st = {k: stats(v) for k, v in spans.items()}
+    aa = abs(1.0 - st["det"]["median"] / st["det_aa"]["median"])
 
     # Per-kernel HIP-event timing of the same K steps, launched eagerly. The
     # GPU is first parked on a sleep kernel so that the host queues all K
@@ -178,26 +375,40 @@ def time_steps(args, torch, rn, _lib, dev, sets, fwd, step, n_fwd, has_bwd, bwd_
         n, ms = timers[idx]
         return (ms / n * 1e3) if n else None
 
-    fwd_us = avg_us(_lib.RMSN_TIMER_FWD)
-    bwd_row_us = avg_us(_lib.RMSN_TIMER_BWD_ROW)
-    reduce_us = avg_us(_lib.RMSN_TIMER_DW_REDUCE)
-    small_us = avg_us(_lib.RMSN_TIMER_BWD_SMALL)
-    if not has_bwd:
-        dom_name, dom_us, dom_bytes = "fwd", fwd_us, fwd_b
-    elif bwd_row_us is not None:
-        dom_name, dom_us, dom_bytes = "bwd_row", bwd_row_us, bwd_row_b
-    else:
-        dom_name, dom_us, dom_bytes = "bwd_small", small_us, bwd_b
-    achieved = dom_bytes / (dom_us * 1e-6) / 1e9
+    ku = {"fwd": avg_us(_lib.RMSN_TIMER_FWD), "bwd_row": avg_us(_lib.RMSN_TIMER_BWD_ROW),
+          "dw_reduce": avg_us(_lib.RMSN_TIMER_DW_REDUCE), "bwd_small": avg_us(_lib.RMSN_TIMER_BWD_SMALL)}
+    sb = wk.step_bytes(op)
+    ms = st["det"]["median"]
+    return {"op": op, "step_bytes": sb, "ms_per_step": ms, "stats": st, "aa_noise": aa,
+            "value": gbps(sb, ms), "kernel_us": ku, "t_issue_ms": t_issue * 1e3 / K, "K": K, "W": W}
 
-    fwd_gbps = fwd_b / (fwd_us * 1e-6) / 1e9 if fwd_us else None
-    bwd_us = (bwd_row_us or 0.0) + (reduce_us or 0.0) if bwd_row_us else small_us
-    bwd_gbps = bwd_b / (bwd_us * 1e-6) / 1e9 if bwd_us else None
 
-    return dict(fwd_us=fwd_us, bwd_row_us=bwd_row_us, reduce_us=reduce_us, small_us=small_us,
-                dom_name=dom_name, dom_bytes=dom_bytes, achieved=achieved, ms_per_step=ms_per_step,
-                value=value, walls=walls, walls_nd=walls_nd, gpu_ms=gpu_ms, t_issue=t_issue, K=K,
-                W=W, median=median, fwd_gbps=fwd_gbps, bwd_gbps=bwd_gbps)
+def dominant(wk, op, m):
+    """The dominant kernel of a step: (name, algorithmic bytes, mean us)."""
+    fwd_b, bwd_row_b, bwd_b = wk.bytes
+    ku = m["kernel_us"]
+    if op == "fwd+bwd_recompute":
+        bwd_row_b -= 4 * wk.rows
+        bwd_b -= 4 * wk.rows
+    if op == "fwd":
+        return "fwd", fwd_b, ku["fwd"]
+    if ku["bwd_row"] is not None:
+        return "bwd_row", bwd_row_b, ku["bwd_row"]
+    return "bwd_small", bwd_b, ku["bwd_small"]
+
+
+def op_summary(wk, op, m):
+    st = m["stats"]["det"]
+    name, nb, us = dominant(wk, op, m)
+    out = {"GBps": round(m["value"], 1), "pct_of_hbm_peak": round(100 * m["value"] / HBM_PEAK_GBPS, 2),
+           "ms_per_step": round(m["ms_per_step"], 5), "p10": round(st["p10"], 5),
+           "p90": round(st["p90"], 5), "aa_noise": round(m["aa_noise"], 4),
+           "kernel_us": {k: (round(v, 3) if v is not None else None) for k, v in m["kernel_us"].items()},
+           "roofline_kernel": name,
+           "roofline_frac": round(gbps(nb, us * 1e-3) / HBM_PEAK_GBPS, 4) if us else None}
+    if "nondet" in m["stats"]:
+        out["nondet_ms_per_step"] = round(m["stats"]["nondet"]["median"], 5)
+    return out
 
 
 def cpu_baseline(args, rows, step_bytes, op, oracle_rows):
@@ -235,150 +446,62 @@ def cpu_baseline(args, rows, step_bytes, op, oracle_rows):
                               "sample": f"{reps_1} repetition(s) in {el_1:.1f} s"}}
 
 
-def result_line(args, metric, op, value, t, step_bytes, config, traffic, cpu, route=None):
-    K = t["K"]
-    walls, walls_nd, median = t["walls"], t["walls_nd"], t["median"]
-    return {
-        "metric": metric,
-        "value": round(value, 2),
-        "unit": "GB/s",
-        "n_gpus": 1,
-        "steps": K,
-        "warmup": t["W"],
-        "ms_per_step": round(t["ms_per_step"], 5),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        # the arithmetic: FP32 row math with FP64 sums (rstd, dw); BF16 and the
-        # weight dtype are storage only
-        "dtype": "f32",
-        "io_dtype": "bf16 activations and gradients, weight as configured",
-        "data": "synthetic",
-        "config": config,
-        "replay_ms_per_step": {"median": round(t["ms_per_step"], 5), "min": round(walls[0] / K, 5),
-                               "max": round(walls[-1] / K, 5), "replays": len(walls)},
-        "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBPS, 2),
-        "fwd_GBps": round(t["fwd_gbps"], 1) if t["fwd_gbps"] else None,
-        "bwd_GBps": round(t["bwd_gbps"], 1) if t["bwd_gbps"] else None,
-        "nondeterministic": ({"ms_per_step": round(median(walls_nd) / K, 5),
-                              "value": round(step_bytes / (median(walls_nd) / K * 1e-3) / 1e9, 2)}
-                             if walls_nd else None),
-        "kernel_us": {"fwd": t["fwd_us"], "bwd_row": t["bwd_row_us"], "dw_reduce": t["reduce_us"],
-                      "bwd_small": t["small_us"]},
-        "graph_gpu_ms": round(t["gpu_ms"], 4),
-        "eager_host_issue_ms_per_step": round(t["t_issue"] * 1e3 / K, 5),
-        "roofline": {"bound": "hbm", "kernel": t["dom_name"], "achieved": round(t["achieved"], 1),
-                     "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(t["achieved"] / HBM_PEAK_GBPS, 4),
-                     "traffic": traffic, "algorithmic_bytes": t["dom_bytes"]},
-        "cpu_baseline": cpu,
-        "route": route,
-    }
-
-
-def bench_layernorm(args, np, torch, rn, _lib, lib, synth, dev, d16) -> int:
-    P = ctypes.c_void_p
-    op = args.op
-    if op not in ("fwd+bwd", "fwd", "bwd", "2xfwd+bwd"):
-        print("--norm layernorm takes --op fwd+bwd, fwd, bwd or 2xfwd+bwd", file=sys.stderr)
-        return 2
-    if args.config is None:
-        args.config = DEFAULT_LN_CONFIG
-    wl = synth.ln_config(args.config, seed=args.seed)
-    T, H = wl.T, wl.H
-    sw = 2 if wl.gamma.dtype == "bf16" else 4
-    wdt = _lib.RMSN_BF16 if sw == 2 else _lib.RMSN_F32
-    fwd_b, bwd_row_b, bwd_b = ln_algorithmic_bytes(T, H, sw)
-    n_fwd = {"fwd+bwd": 1, "fwd": 1, "bwd": 0, "2xfwd+bwd": 2}[op]
-    has_bwd = op != "fwd"
-    step_bytes = n_fwd * fwd_b + (bwd_b if has_bwd else 0)
-
-    def wdev(wt):
-        return d16(wt.bits) if wt.dtype == "bf16" else torch.from_numpy(wt.f32.copy()).to(dev)
-
-    gam, bet = wdev(wl.gamma), wdev(wl.beta)
-    x0, dy0 = d16(wl.x), d16(wl.dy)
-    per_set = 4 * T * H * 2
-    n_sets = int(min(16, max(2, math.ceil((1 << 30) / per_set))))
-    sets = []
-    for _ in range(n_sets):
-        sets.append(dict(x=x0.clone(), dy=dy0.clone(), y=torch.empty_like(x0), dx=torch.empty_like(x0),
-                         mean=torch.empty(T, dtype=torch.float32, device=dev),
-                         rstd=torch.empty(T, dtype=torch.float32, device=dev),
-                         dg=torch.empty(H, dtype=torch.float32, device=dev),
-                         db=torch.empty(H, dtype=torch.float32, device=dev)))
-    del x0, dy0
-    ws = {}
-    for det in (0, 1):
-        nb = max(lib.layernorm_bwd_workspace_bytes(T, H, wdt, det), 256)
-        raw = torch.empty(nb + 256, dtype=torch.uint8, device=dev)
-        ws[det] = (raw, P(raw.data_ptr() + (-raw.data_ptr()) % 256), nb)
-    eps = ctypes.c_float(wl.eps)
-
-    def fwd(s, stream):
-        _lib.check(lib.layernorm_fwd(P(s["x"].data_ptr()), P(gam.data_ptr()), P(bet.data_ptr()), wdt,
-                                     eps, P(s["y"].data_ptr()), P(s["mean"].data_ptr()),
-                                     P(s["rstd"].data_ptr()), T, H, stream))
-
-    def bwd(s, det, stream):
-        _, wsp, nb = ws[det]
-        _lib.check(lib.layernorm_bwd(P(s["dy"].data_ptr()), P(s["x"].data_ptr()),
-                                     P(s["mean"].data_ptr()), P(s["rstd"].data_ptr()),
-                                     P(gam.data_ptr()), wdt, det, P(s["dx"].data_ptr()),
-                                     P(s["dg"].data_ptr()), P(s["db"].data_ptr()), T, H, wsp, nb,
-                                     stream))
-
-    def step(s, det, stream):
-        for _ in range(n_fwd):
-            fwd(s, stream)
-        if has_bwd:
-            bwd(s, det, stream)
-
-    t = time_steps(args, torch, rn, _lib, dev, sets, fwd, step, n_fwd, has_bwd, ["dx", "dg", "db"],
-                   step_bytes, fwd_b, bwd_row_b, bwd_b)
-    cpu = None
-    if not args.no_cpu_baseline:
-        import oracle
+def oracle_step(wk, op):
+    """The oracle's work of one step on rows [lo, hi) (test infrastructure,
+    imported only for the CPU baseline)."""
+    import oracle
+    wl = wk.wl
+    n_fwd, has_bwd, rc = wk.n_fwd(op), op != "fwd", op == "fwd+bwd_recompute"
+    if wk.norm == "layernorm":
         g64, b64 = wl.gamma.f64, wl.beta.f64
         mu_all, rs_all, _ = oracle.ln_fwd(wl.x, g64, b64, wl.eps, want_y=False)
 
-        def oracle_rows(lo, hi):
+        def rows_fn(lo, hi):
             mu, rs = mu_all[lo:hi], rs_all[lo:hi]
             for _ in range(n_fwd):
                 mu, rs, _ = oracle.ln_fwd(wl.x[lo:hi], g64, b64, wl.eps)
             if has_bwd:
                 oracle.ln_bwd(wl.dy[lo:hi], wl.x[lo:hi], mu, rs, g64)
+        return rows_fn
+    xo = wl.x if wl.r is None else oracle.residual_add(wl.x, wl.r)
+    w64 = wl.w.f64
+    r_all, _ = oracle.fwd(xo, w64, wl.eps, want_y=False)
 
-        cpu = cpu_baseline(args, T, step_bytes, op, oracle_rows)
-    config = {"workload": args.config, "norm": "layernorm", "op": op, "T": T, "H": H,
-              "w_dtype": wl.gamma.dtype, "deterministic": True, "global_batch": T, "seq_len": T,
-              "parallelism": "none (1 GPU)", "buffer_sets": n_sets}
-    traffic = None
-    tr_path = os.path.join(ROOT, "profiles", f"traffic_{args.config}.json")
-    if os.path.exists(tr_path) and op == "fwd+bwd":
-        from bwd_rmsnorm_fwd_02_amd import build as _b
-        rec = json.load(open(tr_path))
-        if rec.get("source_hash") == _b.source_hash() and t["dom_name"] in rec.get("kernels", {}):
-            traffic = rec["kernels"][t["dom_name"]]["bytes_per_launch"]
-    wt = torch.bfloat16 if wl.gamma.dtype == "bf16" else torch.float32
-    route = {"fwd": rn.rmsnorm_route_query("ln_fwd", T, H, wt),
-             "bwd": rn.rmsnorm_route_query("ln_bwd", T, H, wt)}
-    out = result_line(args, f"LayerNorm {op} effective HBM GB/s, per (T,H)", op, t["value"], t,
-                      step_bytes, config, traffic, cpu, route)
-    print(json.dumps(out), flush=True)
-    return 0
+    def rows_fn(lo, hi):
+        r64 = r_all[lo:hi]
+        for _ in range(n_fwd):
+            r64, _ = oracle.fwd(xo[lo:hi], w64, wl.eps)
+        if rc:
+            r64, _ = oracle.fwd(xo[lo:hi], w64, wl.eps, want_y=False)
+        if has_bwd:
+            oracle.bwd(wl.dy[lo:hi], xo[lo:hi], r64, w64)
+    return rows_fn
+
+
+def traffic_for(config, dom_name):
+    tr_path = os.path.join(ROOT, "profiles", f"traffic_{config}.json")
+    if not os.path.exists(tr_path):
+        return None
+    from bwd_rmsnorm_fwd_02_amd import build as _b
+    rec = json.load(open(tr_path))
+    if rec.get("source_hash") == _b.source_hash() and dom_name in rec.get("kernels", {}):
+        return rec["kernels"][dom_name]["bytes_per_launch"]
+    return None
 
 
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=400)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=20, help="steps per graph replay (K)")
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--norm", choices=("rmsnorm", "layernorm"), default="rmsnorm")
     ap.add_argument("--config", default=None)
     ap.add_argument("--op", choices=OPS, default="fwd+bwd")
-    ap.add_argument("--replays", type=int, default=5)
+    ap.add_argument("--replays", type=int, default=201, help="replays per graph")
+    ap.add_argument("--rounds", type=int, default=3, help="interleaved rounds the replays are split over")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-per-config", action="store_true",
+                    help="time only the chosen workload, not every workload of its family")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="seconds of oracle work for each of the two CPU runs")
     ap.add_argument("--cpu-threads", type=int, default=0,
@@ -416,156 +539,127 @@ def main() -> int:
         print(json.dumps({"copy_calibration_bytes": n * 2, "launches": 10}), flush=True)
         return 0
 
-    P = ctypes.c_void_p
-    op = args.op
-
-    def d16(bits):
-        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
-
-    if args.norm == "layernorm":
-        return bench_layernorm(args, np, torch, rn, _lib, lib, synth, dev, d16)
+    ln = args.norm == "layernorm"
+    if ln and args.op not in ("fwd+bwd", "fwd", "bwd", "2xfwd+bwd"):
+        print("--norm layernorm takes --op fwd+bwd, fwd, bwd or 2xfwd+bwd", file=sys.stderr)
+        return 2
     if args.config is None:
-        args.config = DEFAULT_CONFIG
-    wl = synth.config(args.config, seed=args.seed)
-    rows, H, T, heads = wl.rows, wl.H, wl.T, wl.heads
-    residual = wl.r is not None
-    with_dres = wl.dres is not None
-    sw = 2 if wl.w.dtype == "bf16" else 4
-    wdt = _lib.RMSN_BF16 if wl.w.dtype == "bf16" else _lib.RMSN_F32
-    fwd_b, bwd_row_b, bwd_b = algorithmic_bytes(rows, H, sw, residual, with_dres)
-    rc = op == "fwd+bwd_recompute"
-    if rc and residual:
+        args.config = DEFAULT_LN_CONFIG if ln else DEFAULT_CONFIG
+    prepare = prepare_layernorm if ln else prepare_rmsnorm
+    family = list(synth.LN_CONFIGS) if ln else list(synth.CONFIGS)
+
+    def progress(msg):
+        print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+    # ---------------- the chosen workload and op
+    progress(f"{args.config}: generating inputs")
+    wk = prepare(args.config, args.seed, torch, np, synth, _lib, lib, dev)
+    op = args.op
+    if op == "fwd+bwd_recompute" and wk.residual:
         print("--op fwd+bwd_recompute covers the plain and per-head forms only", file=sys.stderr)
         return 2
-    if rc:  # the recompute backward reads no rstd
-        bwd_row_b -= 4 * rows
-        bwd_b -= 4 * rows
-    n_fwd = {"fwd+bwd": 1, "fwd": 1, "bwd": 0, "2xfwd+bwd": 2, "fwd+bwd_recompute": 1}[op]
-    has_bwd = op != "fwd"
-    step_bytes = n_fwd * fwd_b + (bwd_b if has_bwd else 0)
-
-    w = d16(wl.w.bits) if wl.w.dtype == "bf16" else torch.from_numpy(wl.w.f32.copy()).to(dev)
-    x0 = d16(wl.xbuf if wl.xbuf is not None else wl.x)
-    dy0 = d16(wl.dy)
-    r0 = d16(wl.r) if residual else None
-    dres0 = d16(wl.dres) if with_dres else None
-
-    # buffer sets: the whole cycle spans >= 1 GiB so steps run from HBM
-    per_set = x0.numel() * 2 + dy0.numel() * 2 + 2 * rows * H * 2 * (2 if residual else 1)
-    n_sets = int(min(16, max(2, math.ceil((1 << 30) / per_set))))
-    sets = []
-    for i in range(n_sets):
-        s = dict(x=x0.clone(), dy=dy0.clone(), y=torch.empty(rows, H, dtype=torch.bfloat16, device=dev),
-                 # the strided form's gap columns are never written: zero them so
-                 # the replay check (which zeroes outputs first) sees the same gap
-                 dx=torch.zeros_like(x0) if wl.xbuf is not None else torch.empty(rows, H, dtype=torch.bfloat16, device=dev),
-                 rstd=torch.empty(rows, dtype=torch.float32, device=dev),
-                 dw=torch.empty(H, dtype=torch.float32, device=dev))
-        if residual:
-            s["r"] = r0.clone()
-            s["h"] = torch.empty(rows, H, dtype=torch.bfloat16, device=dev)
-            s["dres"] = dres0.clone() if with_dres else None
-        sets.append(s)
-    del x0, dy0, r0, dres0
-
-    # separate workspaces: the deterministic partials, and the zero-filled
-    # accumulator the non-deterministic kernels keep zero-filled
-    ws_bytes_det = max(lib.rmsnorm_bwd_workspace_bytes(rows, H, wdt, 1), 256)
-    ws_bytes_nd = max(lib.rmsnorm_bwd_workspace_bytes(rows, H, wdt, 0), 256)
-    ws_det_raw = torch.empty(ws_bytes_det + 256, dtype=torch.uint8, device=dev)
-    ws_nd_raw = torch.zeros(ws_bytes_nd + 256, dtype=torch.uint8, device=dev)
-    ws_det = ws_det_raw[(-ws_det_raw.data_ptr()) % 256:]
-    ws_nd = ws_nd_raw[(-ws_nd_raw.data_ptr()) % 256:]
-    ws_arg = {1: (P(ws_det.data_ptr()), ws_bytes_det), 0: (P(ws_nd.data_ptr()), ws_bytes_nd)}
-
-    if wl.xbuf is not None:
-        xv = _lib.View(T, heads, H, wl.x_stride_t, wl.x_stride_h)
-    else:
-        xv = _lib.View(T, heads, H, heads * H, H)
-    cv = _lib.View(T, heads, H, heads * H, H)
-
-    dxv = xv if wl.xbuf is not None else cv
-
-    def fwd(s, stream):
-        if residual:
-            _lib.check(lib.rmsnorm_residual_fwd(P(s["x"].data_ptr()), P(s["r"].data_ptr()),
-                                                P(w.data_ptr()), wdt, ctypes.c_float(wl.eps),
-                                                P(s["h"].data_ptr()), P(s["y"].data_ptr()),
-                                                P(s["rstd"].data_ptr()), rows, H, stream))
-        else:
-            _lib.check(lib.rmsnorm_fwd_strided(P(s["x"].data_ptr()), xv, P(w.data_ptr()), wdt,
-                                               ctypes.c_float(wl.eps), P(s["y"].data_ptr()), cv,
-                                               P(s["rstd"].data_ptr()), stream))
-
-    def bwd(s, det: int, stream):
-        wsp, ws_bytes = ws_arg[det]
-        if residual:
-            _lib.check(lib.rmsnorm_residual_bwd(P(s["dy"].data_ptr()), P(s["h"].data_ptr()),
-                                                P(s["dres"].data_ptr()) if with_dres else None,
-                                                P(s["rstd"].data_ptr()), P(w.data_ptr()), wdt, det,
-                                                P(s["dx"].data_ptr()), P(s["dw"].data_ptr()), rows, H,
-                                                wsp, ws_bytes, stream))
-        elif rc:
-            _lib.check(lib.rmsnorm_bwd_recompute(P(s["dy"].data_ptr()), cv, P(s["x"].data_ptr()), xv,
-                                                 P(w.data_ptr()), wdt, ctypes.c_float(wl.eps), det,
-                                                 P(s["dx"].data_ptr()), dxv, P(s["dw"].data_ptr()),
-                                                 wsp, ws_bytes, stream))
-        else:
-            _lib.check(lib.rmsnorm_bwd_strided(P(s["dy"].data_ptr()), cv, P(s["x"].data_ptr()), xv,
-                                               P(s["rstd"].data_ptr()), P(w.data_ptr()), wdt, det,
-                                               P(s["dx"].data_ptr()), dxv, P(s["dw"].data_ptr()),
-                                               wsp, ws_bytes, stream))
-
-    def step(s, det: int, stream):
-        for _ in range(n_fwd):
-            fwd(s, stream)
-        if has_bwd:
-            bwd(s, det, stream)
-
-    t = time_steps(args, torch, rn, _lib, dev, sets, fwd, step, n_fwd, has_bwd, ["dx", "dw"],
-                   step_bytes, fwd_b, bwd_row_b, bwd_b)
-    dom_name, value = t["dom_name"], t["value"]
-
-    traffic = None
-    tr_path = os.path.join(ROOT, "profiles", f"traffic_{args.config}.json")
-    if os.path.exists(tr_path) and op == "fwd+bwd":
-        from bwd_rmsnorm_fwd_02_amd import build as _b
-        rec = json.load(open(tr_path))
-        if rec.get("source_hash") == _b.source_hash() and dom_name in rec.get("kernels", {}):
-            traffic = rec["kernels"][dom_name]["bytes_per_launch"]
-
+    progress(f"{args.config} {op}: timing")
+    m = measure_op(args, torch, rn, _lib, dev, wk, op)
+    cold = None
+    if op != "fwd" and op != "bwd":
+        progress(f"{args.config} bwd alone: timing (cold backward)")
+        cold = measure_op(args, torch, rn, _lib, dev, wk, "bwd", nondet=False)
+    dom_name, dom_bytes, dom_us = dominant(wk, op, m)
+    achieved = gbps(dom_bytes, dom_us * 1e-3)
+    frac_cold = None
+    if cold is not None and dom_name == "bwd_row" and cold["kernel_us"]["bwd_row"]:
+        frac_cold = gbps(dom_bytes, cold["kernel_us"]["bwd_row"] * 1e-3) / HBM_PEAK_GBPS
     cpu = None
     if not args.no_cpu_baseline:
-        import oracle
-        # the same work as one step: the forward (n_fwd times; the recompute
-        # backward is the forward's statistics plus the backward), then the
-        # backward at the oracle's rstd
-        xo = wl.x if not residual else oracle.residual_add(wl.x, wl.r)
-        w64 = wl.w.f64
-        r_all, _ = oracle.fwd(xo, w64, wl.eps, want_y=False)
+        progress("cpu baseline (oracle)")
+        cpu = cpu_baseline(args, wk.rows, wk.step_bytes(op), op, oracle_step(wk, op))
+    wt = torch.bfloat16 if wk.wdtype == "bf16" else torch.float32
+    if ln:
+        route = {"fwd": rn.rmsnorm_route_query("ln_fwd", wk.rows, wk.H, wt),
+                 "bwd": rn.rmsnorm_route_query("ln_bwd", wk.rows, wk.H, wt)}
+    else:
+        route = {"fwd": rn.rmsnorm_route_query("fwd", wk.rows, wk.H, wt, residual=wk.residual),
+                 "bwd": rn.rmsnorm_route_query("bwd", wk.rows, wk.H, wt, residual=wk.residual,
+                                               recompute=(op == "fwd+bwd_recompute"))}
+    head_rows, head_T, head_heads, head_H = wk.rows, wk.T, wk.heads, wk.H
+    head_res, head_wdt, n_sets = wk.residual, wk.wdtype, len(wk.sets)
+    per_config = {}
+    if op == "fwd+bwd":
+        per_config[args.config] = {"fwd+bwd": op_summary(wk, op, m)}
+        if cold is not None:
+            per_config[args.config]["bwd"] = op_summary(wk, "bwd", cold)
+    del wk
+    torch.cuda.empty_cache()
 
-        def oracle_rows(lo, hi):
-            r64 = r_all[lo:hi]
-            for _ in range(n_fwd):
-                r64, _ = oracle.fwd(xo[lo:hi], w64, wl.eps)
-            if rc:
-                r64, _ = oracle.fwd(xo[lo:hi], w64, wl.eps, want_y=False)
-            if has_bwd:
-                oracle.bwd(wl.dy[lo:hi], xo[lo:hi], r64, w64)
+    # ---------------- every workload of the family: fwd, bwd, fwd+bwd
+    if not args.no_per_config:
+        for name in family:
+            progress(f"per-config {name}: generating inputs")
+            w2 = prepare(name, args.seed, torch, np, synth, _lib, lib, dev)
+            entry = per_config.setdefault(name, {})
+            for o in ("fwd+bwd", "bwd", "fwd"):
+                if o in entry:
+                    continue
+                progress(f"per-config {name} {o}: timing")
+                entry[o] = op_summary(w2, o, measure_op(args, torch, rn, _lib, dev, w2, o))
+            if "bwd" in entry and entry["bwd"]["roofline_kernel"] == "bwd_row":
+                entry["fwd+bwd"]["roofline_frac_cold_bwd"] = entry["bwd"]["roofline_frac"]
+            del w2
+            torch.cuda.empty_cache()
 
-        cpu = cpu_baseline(args, rows, step_bytes, op, oracle_rows)
-
-    config = {"workload": args.config, "op": op, "T": T, "heads": heads, "H": H,
-              "w_dtype": wl.w.dtype, "residual": residual, "deterministic": True,
-              "global_batch": rows, "seq_len": T, "parallelism": "none (1 GPU)",
-              "buffer_sets": n_sets}
-    metric = METRIC if op == "fwd+bwd" else f"RMSNorm {op} effective HBM GB/s, per (T,H)"
-    # the launch shapes, partition and load policy the route chose (host-side query)
-    wt = torch.bfloat16 if wl.w.dtype == "bf16" else torch.float32
-    route = {"fwd": rn.rmsnorm_route_query("fwd", rows, H, wt, residual=residual),
-             "bwd": rn.rmsnorm_route_query("bwd", rows, H, wt, residual=residual,
-                                           recompute=(op == "fwd+bwd_recompute"))}
-    out = result_line(args, metric, op, value, t, step_bytes, config, traffic, cpu, route)
+    K = m["K"]
+    st = m["stats"]
+    value = m["value"]
+    metric = (METRIC if op == "fwd+bwd" else f"RMSNorm {op} effective HBM GB/s, per (T,H)")
+    if ln:
+        metric = f"LayerNorm {op} effective HBM GB/s, per (T,H)"
+    config = {"workload": args.config, "norm": args.norm, "op": op, "T": head_T, "heads": head_heads,
+              "H": head_H, "w_dtype": head_wdt, "residual": head_res, "deterministic": True,
+              "global_batch": head_rows, "seq_len": head_T, "parallelism": "none (1 GPU)",
+              "buffer_sets": n_sets, "steps_per_replay": K}
+    out = {
+        "metric": metric,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": m["W"],
+        "ms_per_step": round(m["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        # the arithmetic: FP32 row math with FP64 sums (rstd, dw); BF16 and the
+        # weight dtype are storage only
+        "dtype": "f32",
+        "io_dtype": "bf16 activations and gradients, weight as configured",
+        "data": "synthetic",
+        "config": config,
+        "p10": round(st["det"]["p10"], 5),
+        "p90": round(st["det"]["p90"], 5),
+        "aa_noise": round(m["aa_noise"], 4),
+        "timing": {"replays": st["det"]["replays"], "rounds": args.rounds, "steps_per_replay": K,
+                   "span": "HIP events around each graph replay on the replay stream",
+                   "ms_per_step": {k: {q: round(v, 5) for q, v in s.items() if q != "replays"}
+                                   for k, s in st.items()},
+                   "value_p90_p10_GBps": [round(gbps(m["step_bytes"], st["det"]["p90"]), 1),
+                                          round(gbps(m["step_bytes"], st["det"]["p10"]), 1)]},
+        "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBPS, 2),
+        "nondeterministic": ({"ms_per_step": round(st["nondet"]["median"], 5),
+                              "value": round(gbps(m["step_bytes"], st["nondet"]["median"]), 2),
+                              "route": "the same fixed-order kernels as the deterministic mode"}
+                             if "nondet" in st else None),
+        "kernel_us": m["kernel_us"],
+        "eager_host_issue_ms_per_step": round(m["t_issue_ms"], 5),
+        "roofline": {"bound": "hbm", "kernel": dom_name, "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": traffic_for(args.config, dom_name) if op == "fwd+bwd" else None,
+                     "algorithmic_bytes": dom_bytes,
+                     "frac_cold": round(frac_cold, 4) if frac_cold is not None else None},
+        "cpu_baseline": cpu,
+        "route": route,
+        "per_config": per_config or None,
+    }
     print(json.dumps(out), flush=True)
     return 0
 

@@ -37,9 +37,10 @@ STATUS = {
 
 # Every symbol include/rmsnorm.h declares.
 EXPORTS = [
-    "rmsnorm_fwd", "rmsnorm_fwd_strided", "rmsnorm_residual_fwd",
+    "rmsnorm_fwd", "rmsnorm_fwd_strided", "rmsnorm_residual_fwd", "rmsnorm_residual_fwd_strided",
     "rmsnorm_bwd_workspace_bytes", "rmsnorm_workspace_init", "rmsnorm_bwd",
     "rmsnorm_bwd_strided", "rmsnorm_bwd_recompute", "rmsnorm_residual_bwd",
+    "rmsnorm_residual_bwd_strided",
     "rmsnorm_status_string",
     "rmsnorm_route_query", "rmsnorm_route_override", "rmsnorm_timing_enable",
     "rmsnorm_timing_read", "layernorm_fwd", "layernorm_bwd_workspace_bytes", "layernorm_bwd",
@@ -106,12 +107,15 @@ def load() -> ctypes.CDLL:
         "rmsnorm_fwd": [p, p, i32, f32, p, p, i64, i64, p],
         "rmsnorm_fwd_strided": [p, View, p, i32, f32, p, View, p, p],
         "rmsnorm_residual_fwd": [p, p, p, i32, f32, p, p, p, i64, i64, p],
+        "rmsnorm_residual_fwd_strided": [p, View, p, View, p, i32, f32, p, View, p, View, p, p],
         "rmsnorm_bwd_workspace_bytes": [i64, i64, i32, i32],
         "rmsnorm_workspace_init": [p, sz, p],
         "rmsnorm_bwd": [p, p, p, p, i32, i32, p, p, i64, i64, p, sz, p],
         "rmsnorm_bwd_strided": [p, View, p, View, p, p, i32, i32, p, View, p, p, sz, p],
         "rmsnorm_bwd_recompute": [p, View, p, View, p, i32, f32, i32, p, View, p, p, sz, p],
         "rmsnorm_residual_bwd": [p, p, p, p, p, i32, i32, p, p, i64, i64, p, sz, p],
+        "rmsnorm_residual_bwd_strided": [p, View, p, View, p, View, p, p, i32, i32, p, View, p, p,
+                                         sz, p],
         "rmsnorm_status_string": [i32],
         "rmsnorm_route_query": [i32, i64, i64, i32, i32, i32, ctypes.POINTER(RouteInfo)],
         "rmsnorm_route_override": [i32, ctypes.POINTER(RouteKnobs)],

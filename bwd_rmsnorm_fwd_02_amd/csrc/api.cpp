@@ -147,7 +147,11 @@ int fwd_impl(const void* x, const rmsn_view_t& xv, const void* r, const rmsn_vie
     if ((st = check_shape(xv)) != RMSN_OK) return st;
     if ((st = check_shape(yv)) != RMSN_OK) return st;
     if (!same_shape(xv, yv)) return RMSN_ERR_SHAPE;
-    if (residual && (!same_shape(xv, *rv) || !same_shape(xv, *hv))) return RMSN_ERR_SHAPE;
+    if (residual) {
+        if ((st = check_shape(*rv)) != RMSN_OK) return st;
+        if ((st = check_shape(*hv)) != RMSN_OK) return st;
+        if (!same_shape(xv, *rv) || !same_shape(xv, *hv)) return RMSN_ERR_SHAPE;
+    }
     if ((st = check_eps(eps)) != RMSN_OK) return st;
     const int64_t rows = xv.T * xv.heads;
     if (rows == 0) return RMSN_OK;
@@ -224,7 +228,10 @@ int bwd_impl(const void* dy, const rmsn_view_t& dyv, const void* x, const rmsn_v
     if ((st = check_shape(dyv)) != RMSN_OK) return st;
     if ((st = check_shape(dxv)) != RMSN_OK) return st;
     if (!same_shape(xv, dyv) || !same_shape(xv, dxv)) return RMSN_ERR_SHAPE;
-    if (dres && !same_shape(xv, *resv)) return RMSN_ERR_SHAPE;
+    if (dres) {
+        if ((st = check_shape(*resv)) != RMSN_OK) return st;
+        if (!same_shape(xv, *resv)) return RMSN_ERR_SHAPE;
+    }
     const int64_t rows = xv.T * xv.heads;
     const int64_t H = xv.H;
     if (!dw) return RMSN_ERR_NULL;
@@ -459,6 +466,14 @@ int rmsnorm_residual_fwd(const void* x, const void* r, const void* w, rmsn_dtype
     return fwd_impl(x, v, r ? r : x, &v, h, &v, w, w_dtype, eps, y, v, rstd, stream);
 }
 
+int rmsnorm_residual_fwd_strided(const void* x, rmsn_view_t xv, const void* r, rmsn_view_t rv,
+                                 const void* w, rmsn_dtype_t w_dtype, float eps, void* h,
+                                 rmsn_view_t hv, void* y, rmsn_view_t yv, float* rstd,
+                                 hipStream_t stream) {
+    if (!r && xv.T * xv.heads != 0) return RMSN_ERR_NULL;
+    return fwd_impl(x, xv, r ? r : x, &rv, h, &hv, w, w_dtype, eps, y, yv, rstd, stream);
+}
+
 size_t rmsnorm_bwd_workspace_bytes(int64_t rows, int64_t H, rmsn_dtype_t w_dtype,
                                    int deterministic) {
     // the largest need over the three backward forms
@@ -511,6 +526,15 @@ int rmsnorm_residual_bwd(const void* dy, const void* h, const void* dres, const 
     const rmsn_view_t v = contiguous(T, H);
     return bwd_impl(dy, v, h, v, dres, dres ? &v : nullptr, rstd, w, w_dtype, deterministic, dh, v,
                     dw, workspace, workspace_bytes, kFormResidual, 0.f, stream);
+}
+
+int rmsnorm_residual_bwd_strided(const void* dy, rmsn_view_t dyv, const void* h, rmsn_view_t hv,
+                                 const void* dres, rmsn_view_t dresv, const float* rstd,
+                                 const void* w, rmsn_dtype_t w_dtype, int deterministic, void* dh,
+                                 rmsn_view_t dhv, float* dw, void* workspace,
+                                 size_t workspace_bytes, hipStream_t stream) {
+    return bwd_impl(dy, dyv, h, hv, dres, dres ? &dresv : nullptr, rstd, w, w_dtype, deterministic,
+                    dh, dhv, dw, workspace, workspace_bytes, kFormResidual, 0.f, stream);
 }
 
 int layernorm_fwd(const void* x, const void* gamma, const void* beta, rmsn_dtype_t w_dtype,

@@ -9,13 +9,14 @@
  *             xhat = x*rstd, c_t = mean_j(dy_tj * w_j * xhat_tj),
  *             dx_tj = rstd_t * (dy_tj * w_j - xhat_tj * c_t),
  *             dw_j = sum_t dy_tj * xhat_tj
- * The two backward modes (deterministic = 1 or 0) share the forward and
- * differ only in how the dw column sum over T is reduced. Forms (same page):
- * plain [T, H] rows with BF16 or FP32 weight; a fused residual add
- * (h_new = BF16(h + u), "Key" paragraph); per-head views [T, heads, H]
- * (strided or contiguous) that share one w[H], with dw summed over T and
- * heads. Workload conventions ("Workload" paragraph): y, dx and h_new BF16;
- * rstd and dw FP32.
+ * Both backward modes (deterministic = 1 or 0) run after one and the same
+ * forward; what may differ between them is only the reduction of the dw
+ * column sum over T. Forms (same page, opening description and "Key"): rows
+ * of [T, H] with a weight in BF16 or FP32; a residual add fused ahead of the
+ * norm, whose rounded BF16 sum is both written out and normalised; and
+ * per-head views [T, heads, H], strided or contiguous, all heads sharing one
+ * w[H], with dw summed over T and over the heads. Output dtypes ("Workload"
+ * paragraph): y, dx and the residual sum BF16; rstd and dw FP32.
  *
  * Conventions for every entry point:
  * - All tensor pointers are DEVICE pointers on the current HIP device; the
@@ -97,17 +98,28 @@ int rmsnorm_fwd(const void* x, const void* w, rmsn_dtype_t w_dtype, float eps,
 
 /* Forward over arbitrary views (per-head [T, heads, H], strided or not).
  * x and y views must agree on T, heads and H; rstd has T*heads entries.
- * (Same page: per-head views [T,24,256] strided and [T,4,256] contiguous
- * with a shared w[256].) */
+ * (Same page, opening description: per-head views, 24 heads of 256 in a
+ * strided buffer or 4 heads of 256 contiguous, that share one weight.) */
 int rmsnorm_fwd_strided(const void* x, rmsn_view_t xv, const void* w,
                         rmsn_dtype_t w_dtype, float eps, void* y, rmsn_view_t yv,
                         float* rstd, hipStream_t stream);
 
 /* Fused residual forward on contiguous [T, H]: h = BF16(x + r) is written,
- * then y, rstd = RMSNorm(h). (Same page, "Key": h_new = BF16(h + u).) */
+ * then y, rstd = RMSNorm(h). (Same page, "Key": the fused residual form
+ * rounds the sum of the two BF16 inputs once to BF16.) */
 int rmsnorm_residual_fwd(const void* x, const void* r, const void* w,
                          rmsn_dtype_t w_dtype, float eps, void* h, void* y,
                          float* rstd, int64_t T, int64_t H, hipStream_t stream);
+
+/* The same over views: x, r, h and y each have their own view, and the four
+ * agree on T, heads and H; rstd has T*heads entries. h may be x itself (same
+ * pointer and view); no other output may overlap an input. (Same page,
+ * opening description: the residual form, and the per-head views that share
+ * one weight.) */
+int rmsnorm_residual_fwd_strided(const void* x, rmsn_view_t xv, const void* r, rmsn_view_t rv,
+                                 const void* w, rmsn_dtype_t w_dtype, float eps, void* h,
+                                 rmsn_view_t hv, void* y, rmsn_view_t yv, float* rstd,
+                                 hipStream_t stream);
 
 /* --------------------------------------------------------------- backward */
 
@@ -123,18 +135,25 @@ int rmsnorm_workspace_init(void* workspace, size_t workspace_bytes, hipStream_t 
 
 /* Plain backward on contiguous [T, H]. rstd is the forward's FP32 output.
  * deterministic != 0: dw is bit-identical run to run for the same inputs and
- * does not depend on the device's CU count; deterministic == 0 may reduce dw
- * with atomics. dx is bit-identical between the two modes.
- * (Same page: deterministic=True and =False share the forward and differ
- * only in the backward; dw budget "per element atol 1e-4 + rtol 1e-4 vs
- * FP64" in "Changed windows by reason".) */
+ * does not depend on the device's CU count. deterministic == 0 allows an
+ * order of the dw reduction that may vary between runs; this library's
+ * route table currently serves both values with the same fixed-order
+ * kernels (an atomic reduction measured slower on this part), so today both
+ * modes return the same dw bits. dx is bit-identical between the two modes.
+ * (Same page, opening description: the two modes run one forward and differ
+ * in the backward only; "Changed windows by reason": every dw element must
+ * lie within 1e-4 absolute plus 1e-4 relative of the FP64 result.) */
 int rmsnorm_bwd(const void* dy, const void* x, const float* rstd, const void* w,
                 rmsn_dtype_t w_dtype, int deterministic, void* dx, float* dw,
                 int64_t T, int64_t H, void* workspace, size_t workspace_bytes,
                 hipStream_t stream);
 
 /* Backward over views: dy, x and dx views agree on T, heads and H; dw[H]
- * sums over T and heads. */
+ * sums over T and heads. dx may be a strided view into a wider buffer; only
+ * the elements the view covers are written. Modes and workspace as in
+ * rmsnorm_bwd. (Same page, opening description: per-head views with 24
+ * heads of 256 in a strided buffer and 4 heads of 256 contiguous, both
+ * modes, one shared w[256].) */
 int rmsnorm_bwd_strided(const void* dy, rmsn_view_t dyv, const void* x, rmsn_view_t xv,
                         const float* rstd, const void* w, rmsn_dtype_t w_dtype,
                         int deterministic, void* dx, rmsn_view_t dxv, float* dw,
@@ -169,6 +188,16 @@ int rmsnorm_residual_bwd(const void* dy, const void* h, const void* dres,
                          const float* rstd, const void* w, rmsn_dtype_t w_dtype,
                          int deterministic, void* dh, float* dw, int64_t T, int64_t H,
                          void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* The same over views: dy, h, dres (when not NULL) and dh each have their
+ * own view, agreeing on T, heads and H; dresv is ignored when dres is NULL;
+ * rstd has T*heads entries; dw sums over T and heads. Modes and workspace as
+ * in rmsnorm_bwd. (Same page, opening description and "Key".) */
+int rmsnorm_residual_bwd_strided(const void* dy, rmsn_view_t dyv, const void* h, rmsn_view_t hv,
+                                 const void* dres, rmsn_view_t dresv, const float* rstd,
+                                 const void* w, rmsn_dtype_t w_dtype, int deterministic, void* dh,
+                                 rmsn_view_t dhv, float* dw, void* workspace,
+                                 size_t workspace_bytes, hipStream_t stream);
 
 /* -------------------------------------------------------------- LayerNorm
  *

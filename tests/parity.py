@@ -30,11 +30,15 @@ U32 = 2.0 ** -24
 
 
 def bf16_ulp(v: np.ndarray) -> np.ndarray:
-    """ULP of BF16 at the magnitude of v (float64), 2^-133 below the normal range."""
+    """ULP of BF16 at the magnitude of v (float64): 2^(e - 7) for the binade
+    exponent e = floor(log2 |v|), read from the float64 exponent field (exact,
+    unlike a rounded log2 at the top of a binade); 2^-133 below the normal
+    range and at zero."""
     a = np.abs(np.asarray(v, np.float64))
-    e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
-    e = np.maximum(e, -126.0)
-    return np.where(a > 0, np.exp2(e - 7.0), 2.0 ** -133)
+    e = ((a.view(np.int64) >> 52) & 0x7FF) - 1023
+    e = np.maximum(e, -126)
+    u = ((e + (1023 - 7)) << 52).view(np.float64)
+    return np.where(a > 0, u, 2.0 ** -133)
 
 
 def to_f64(bits: np.ndarray) -> np.ndarray:

@@ -151,6 +151,42 @@ def test_bwd_recompute_argument_errors():
              _fake(DW), _fake(WS), need, s) == -3
 
 
+@fake_only
+def test_residual_view_argument_errors():
+    A = 0x80000000
+    s = P(0)
+    V = _lib.View
+    T, heads, H = 64, 4, 256
+    c = V(T, heads, H, heads * H, H)
+    X, R, W, Hh, Y, RS = (A + i * 0x1000000 for i in range(6))
+    f = lib.rmsnorm_residual_fwd_strided
+    ok = lambda **k: [_fake(X), k.get("xv", c), _fake(k.get("r", R)) if k.get("r", R) else None,
+                      k.get("rv", c), _fake(W), 1, 1e-6, _fake(k.get("h", Hh)), k.get("hv", c),
+                      _fake(k.get("y", Y)), k.get("yv", c), _fake(RS), s]
+    assert f(*ok(r=0)) == -1
+    assert f(*ok(rv=V(T, heads + 1, H, heads * H, H))) == -3     # views disagree
+    assert f(*ok(hv=V(T, heads, H, -heads * H, H))) == -3        # negative stride
+    assert f(*ok(rv=V(T, heads, H, heads * H + 4, H))) == -4     # stride not 16-byte aligned
+    assert f(*ok(h=R)) == -7                                     # h over r
+    assert f(*ok(y=X + 16)) == -7                                # y overlapping x
+    assert f(*ok(hv=V(T, heads, H, heads * H, H // 2))) == -7    # h rows overlap each other
+    assert f(None, V(0, heads, H, heads * H, H), None, V(0, heads, H, heads * H, H), None, 1, 1e-6,
+             None, V(0, heads, H, heads * H, H), None, V(0, heads, H, heads * H, H), None, s) == 0
+    g = lib.rmsnorm_residual_bwd_strided
+    DY, HH, DR, RS2, W2, DH, DW, WS = (A + 0x8000000 + i * 0x1000000 for i in range(8))
+    need = lib.rmsnorm_bwd_workspace_bytes(T * heads, H, 1, 1)
+    bad = V(T, heads, H, heads * H + 8, H)
+    args = lambda **k: [_fake(DY), c, _fake(HH), c, _fake(k.get("dr", DR)) if k.get("dr", DR) else None,
+                        k.get("drv", c), _fake(RS2), _fake(W2), 1, 1, _fake(k.get("dh", DH)), c,
+                        _fake(DW), _fake(WS), need, s]
+    assert g(*args(drv=V(T, heads, H + 8, heads * H, H))) == -3  # dres view disagrees
+    assert g(*args(drv=V(T, heads, H, -8, H))) == -3             # negative stride
+    assert g(*args(dh=DR)) == -7                                 # dh over dres
+    assert g(*args(dh=HH)) == -7                                 # dh over h
+    # a NULL dres ignores its view
+    assert g(*args(dr=0, drv=bad, dh=HH)) == -7
+
+
 # ------------------------------------------------------------------ routes
 
 def route(op, rows, H, wdt=0, det=1, res=0):

@@ -1,18 +1,28 @@
 """dw accuracy sweep (flashinfer PR "fix(cake_rmsnorm): sm_100a and sm_107a
 dw-accuracy backward routes", section "Changed windows by reason", and the
-"Tests" list of the re-vendoring commit on the same page): three input
-families, the worst over the seeds, token counts on both sides of each route
-edge, both rstd forms, and the FP32-eager criterion. A program fails that
-criterion when its worst dw error exceeds that of the FP32 eager computation
-on the same inputs (FP32 weight) or its median dw error exceeds the eager
-median (either weight dtype). The eager computation is torch in float32 on
-the GPU: dw = sum over t of dy * (x * rstd).
+"Tests" list of the re-vendoring commit on the same page).
 
-Each case prints the worst error as a fraction of the budget.
+The page qualifies a route by sampling every 64th token count of a window
+(and both sides of each edge) with 60, 120 or 240 inputs of each of three
+input families, at both rstd forms, against the dw budget and against the
+FP32 eager computation: a program fails the latter if its largest dw error
+is above the eager one's (FP32 weight) or its median dw error is above the
+eager median (either weight dtype). Here the eager computation is torch in
+float32 on the GPU, dw = sum over t of dy * (x * rstd), at the same FP32
+rstd, and its error is measured against the same FP64 dw.
 
-The pages draw 60, 120 or 240 inputs per family; the default here is five
-seeds per case, to keep the GPU suite short. RMSN_SWEEP_SEEDS=60 runs the
-same cases at the pages' smallest size.
+Sweeps, each case the worst of its inputs (five seeds by default;
+RMSN_SWEEP_SEEDS raises it):
+* every 64th T over [1, 512] plus T 65, around the small-T edge 64 | 65
+  (column tasks below, the row kernel above), at H 4096 with either weight
+  dtype;
+* every 64th T over [7936, 8448] plus T 8193, around the 8192 | 8193 edge
+  where dw partials go from FP32 to FP64, at H 1024 with FP32 weight;
+* one mid-size shape per other width class;
+* 60 N(0,1) inputs at one point on each side of the two edges' upper end
+  (T 65 and T 8193), the page's smallest sample size.
+
+Each case prints its worst error as a fraction of the budget.
 """
 from __future__ import annotations
 
@@ -30,32 +40,28 @@ from tests.test_parity_gpu import DEV, dev_bf16, dev_f32, dev_w
 
 pytestmark = pytest.mark.gpu
 
-SEEDS = range(int(os.environ.get("RMSN_SWEEP_SEEDS", "5")))
+N_SEEDS = int(os.environ.get("RMSN_SWEEP_SEEDS", "5"))
 
-# (T, H, w dtype): both sides of the small-T edge (64 | 65), of the
-# FP32 | FP64 partial switch (8192 | 8193), and mid-size rows of each width
-# class in the route table.
-EDGES = [
-    (64, 256, "f32"), (65, 256, "f32"),
-    (64, 4096, "bf16"), (65, 4096, "bf16"),
-    (8192, 1024, "f32"), (8193, 1024, "f32"),
-    (4097, 2048, "bf16"), (12000, 5120, "f32"),
-    (20000, 256, "bf16"),
-]
+GRID_SMALL = sorted({1, 65} | set(range(64, 513, 64)))          # edge 64 | 65
+GRID_PARTIAL = sorted({8193} | set(range(7936, 8449, 64)))      # edge 8192 | 8193
+
+CASES = ([(T, 4096, wdt) for T in GRID_SMALL for wdt in ("bf16", "f32")]
+         + [(T, 1024, "f32") for T in GRID_PARTIAL]
+         # other width classes of the route table, mid-size rows
+         + [(4097, 2048, "bf16"), (12000, 5120, "f32"), (20000, 256, "bf16")])
 
 
 def _errors(dw, dw64):
     return np.abs(np.asarray(dw, np.float64) - dw64)
 
 
-@pytest.mark.parametrize("family", list(synth.FAMILIES))
-@pytest.mark.parametrize("T,H,wdt", EDGES)
-def test_dw_accuracy_sweep(family, T, H, wdt):
+def _sweep(family, T, H, wdt, n_inputs, seed0=0):
     worst = {True: 0.0, False: 0.0}
     worst_eager = 0.0
     ours_med, eager_med = [], []
     ours_max, eager_max = [], []
-    for seed in SEEDS:
+    for i in range(n_inputs):
+        seed = seed0 + i
         wl = synth.make(T=T, H=H, w_dtype=wdt, seed=1000 * seed + T + H, **synth.FAMILIES[family])
         r64, r32 = oracle_rstd32(wl.x, wl.w.f64, wl.eps)
         _, _, dw64 = oracle.bwd(wl.dy, wl.x, r32.astype(np.float64), wl.w.f64, want_dx=False)
@@ -68,7 +74,8 @@ def test_dw_accuracy_sweep(family, T, H, wdt):
             torch.cuda.synchronize()
             dwn = dw.cpu().numpy()
             e = _errors(dwn, dw64)
-            worst[det] = max(worst[det], float(np.max(e / tol)), float(np.max(_errors(dwn, dw64_i) / tol_i)))
+            worst[det] = max(worst[det], float(np.max(e / tol)),
+                             float(np.max(_errors(dwn, dw64_i) / tol_i)))
             if det:
                 ours_med.append(float(np.median(e)))
                 ours_max.append(float(np.max(e)))
@@ -78,15 +85,28 @@ def test_dw_accuracy_sweep(family, T, H, wdt):
         eager_med.append(float(np.median(ee)))
         eager_max.append(float(np.max(ee)))
         worst_eager = max(worst_eager, float(np.max(ee / tol)))
-        if len(SEEDS) > 5 and (seed + 1) % 20 == 0:
-            print(f"  {family} T={T} H={H}: {seed + 1}/{len(SEEDS)} inputs", flush=True)
-    print(f"family={family} T={T} H={H} w={wdt} inputs={len(SEEDS)}: worst dw err/budget "
+        if n_inputs > 5 and (i + 1) % 20 == 0:
+            print(f"  {family} T={T} H={H}: {i + 1}/{n_inputs} inputs", flush=True)
+    print(f"family={family} T={T} H={H} w={wdt} inputs={n_inputs}: worst dw err/budget "
           f"det {worst[True]:.2e} non-det {worst[False]:.2e}; FP32 eager {worst_eager:.2e}; "
           f"median err ours {np.median(ours_med):.2e} eager {np.median(eager_med):.2e}", flush=True)
     assert worst[True] <= 1.0 and worst[False] <= 1.0
     if wdt == "f32":
         assert max(ours_max) <= max(eager_max), "worst dw error above the FP32 eager reference's"
     assert np.median(ours_med) <= np.median(eager_med), "median dw error above the FP32 eager median"
+
+
+@pytest.mark.parametrize("family", list(synth.FAMILIES))
+@pytest.mark.parametrize("T,H,wdt", CASES)
+def test_dw_accuracy_sweep(family, T, H, wdt):
+    _sweep(family, T, H, wdt, N_SEEDS)
+
+
+@pytest.mark.parametrize("T,H", [(65, 4096), (8193, 1024)])
+def test_dw_accuracy_60_inputs(T, H):
+    """The page's smallest qualifying sample: 60 inputs of the N(0,1) family,
+    just above each edge, FP32 weight (both eager criteria apply)."""
+    _sweep("normal", T, H, "f32", max(60, N_SEEDS), seed0=100)
 
 
 # The pages' top windows: the token counts at which their earlier kernels

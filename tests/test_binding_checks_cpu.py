@@ -1,0 +1,145 @@
+"""The Python binding checks every tensor argument before it hands a pointer
+to the C ABI: dtype, shape, layout and device of inputs, of caller-supplied
+outputs and of the workspace. These run on CPU tensors: a call whose
+arguments are all well formed stops at the last check (the tensors must live
+on a ROCm device), and any malformed argument stops earlier, naming itself.
+Nothing here reaches the library's compute entry points.
+"""
+from __future__ import annotations
+
+import pytest
+import torch
+
+import bwd_rmsnorm_fwd_02_amd as rn
+
+T, HEADS, H = 6, 3, 64
+BF, F32 = torch.bfloat16, torch.float32
+
+
+def act(*shape):
+    return torch.zeros(shape or (T, H), dtype=BF)
+
+
+def vec(n, dtype=F32):
+    return torch.zeros(n, dtype=dtype)
+
+
+def expect(exc, fn, *args, match=None, **kw):
+    with pytest.raises(exc, match=match):
+        fn(*args, **kw)
+
+
+DEVICE_MSG = "ROCm device"
+
+
+# ------------------------------------------------------------- forward
+
+def test_fwd_checks():
+    x, w = act(), vec(H)
+    expect(TypeError, rn.rmsnorm_fwd, x, w, match=DEVICE_MSG)            # well formed
+    expect(TypeError, rn.rmsnorm_fwd, x.float(), w, match="x must be bfloat16")
+    expect(ValueError, rn.rmsnorm_fwd, act().t(), vec(T), match="x must be a contiguous")
+    expect(ValueError, rn.rmsnorm_fwd, x, vec(H - 8), match="w has shape")
+    expect(TypeError, rn.rmsnorm_fwd, x, vec(H, torch.float16), match="weight dtype")
+    expect(ValueError, rn.rmsnorm_fwd, x, vec(2 * H)[::2], match="w must be contiguous")
+    expect(ValueError, rn.rmsnorm_fwd, x, w, y=act(T, H + 8), match="y has shape")
+    expect(ValueError, rn.rmsnorm_fwd, x, w, y=act(H, T).t(), match="y must be contiguous")
+    expect(TypeError, rn.rmsnorm_fwd, x, w, rstd=vec(T, BF), match="rstd must be float32")
+    expect(ValueError, rn.rmsnorm_fwd, x, w, rstd=vec(T - 1), match="rstd has 5 elements")
+    expect(TypeError, rn.rmsnorm_fwd, x, w, rstd=[0.0] * T, match="rstd must be a torch.Tensor")
+
+
+def test_fwd_strided_checks():
+    buf = act(T, 8 * H)
+    xv = buf[:, : HEADS * H].unflatten(1, (HEADS, H))
+    w = vec(H)
+    expect(TypeError, rn.rmsnorm_fwd_strided, xv, w, match=DEVICE_MSG)
+    expect(ValueError, rn.rmsnorm_fwd_strided, act(T, H, HEADS).transpose(1, 2), w,
+           match="last dimension must be contiguous")
+    expect(ValueError, rn.rmsnorm_fwd_strided, xv, w, y=act(T, HEADS + 1, H), match="y has shape")
+    expect(ValueError, rn.rmsnorm_fwd_strided, xv, w, rstd=vec(T), match="rstd has 6 elements")
+    expect(ValueError, rn.rmsnorm_fwd_strided, xv, vec(H + 8), match="w has shape")
+
+
+def test_residual_fwd_checks():
+    x, r, w = act(), act(), vec(H, BF)
+    expect(TypeError, rn.rmsnorm_residual_fwd, x, r, w, match=DEVICE_MSG)
+    expect(ValueError, rn.rmsnorm_residual_fwd, x, act(T + 1, H), w, match="r has shape")
+    expect(TypeError, rn.rmsnorm_residual_fwd, x, r.float(), w, match="r must be bfloat16")
+    expect(ValueError, rn.rmsnorm_residual_fwd, x, act(H, T).t(), w, match="r must be contiguous")
+    expect(ValueError, rn.rmsnorm_residual_fwd, x, r, w, h=act(T, 2 * H), match="h has shape")
+    expect(ValueError, rn.rmsnorm_residual_fwd, x, r, w, y=act(T - 1, H), match="y has shape")
+    expect(ValueError, rn.rmsnorm_residual_fwd, x, r, w, rstd=vec(2 * T), match="rstd has")
+
+
+def test_residual_fwd_strided_checks():
+    x = act(T, HEADS, H)
+    w = vec(H)
+    expect(TypeError, rn.rmsnorm_residual_fwd_strided, x, act(T, HEADS, H), w, match=DEVICE_MSG)
+    expect(ValueError, rn.rmsnorm_residual_fwd_strided, x, act(T, HEADS * H), w, match="r has shape")
+    expect(ValueError, rn.rmsnorm_residual_fwd_strided, x, x, w, h=act(T, HEADS, 2 * H),
+           match="h has shape")
+
+
+# ------------------------------------------------------------ backward
+
+def test_bwd_checks():
+    dy, x, rs, w = act(), act(), vec(T), vec(H)
+    expect(TypeError, rn.rmsnorm_bwd, dy, x, rs, w, match=DEVICE_MSG)
+    # a transposed (non-contiguous) gradient of the right shape
+    expect(ValueError, rn.rmsnorm_bwd, act(H, T).t(), x, rs, w, match="dy must be contiguous")
+    expect(ValueError, rn.rmsnorm_bwd, act(T + 2, H), x, rs, w, match="dy has shape")
+    expect(TypeError, rn.rmsnorm_bwd, dy.half(), x, rs, w, match="dy must be bfloat16")
+    expect(ValueError, rn.rmsnorm_bwd, dy, x, vec(T - 1), w, match="rstd has")
+    expect(TypeError, rn.rmsnorm_bwd, dy, x, vec(T, BF), w, match="rstd must be float32")
+    expect(ValueError, rn.rmsnorm_bwd, dy, x, vec(2 * T)[::2], w, match="rstd must be contiguous")
+    expect(ValueError, rn.rmsnorm_bwd, dy, x, rs, vec(H // 2), match="w has shape")
+    expect(ValueError, rn.rmsnorm_bwd, dy, x, rs, w, dx=act(T, H - 8), match="dx has shape")
+    expect(ValueError, rn.rmsnorm_bwd, dy, x, rs, w, dw=vec(H - 1), match="dw has")
+    expect(TypeError, rn.rmsnorm_bwd, dy, x, rs, w, dw=vec(H, torch.float64), match="dw must be float32")
+    expect(ValueError, rn.rmsnorm_bwd, dy, x, rs, w, workspace=torch.zeros(64, 64, dtype=torch.uint8).t(),
+           match="workspace must be contiguous")
+
+
+def test_bwd_strided_and_recompute_checks():
+    buf = act(T, 8 * H)
+    xv = buf[:, : HEADS * H].unflatten(1, (HEADS, H))
+    dy, rs, w = act(T, HEADS, H), vec(T * HEADS), vec(H)
+    expect(TypeError, rn.rmsnorm_bwd_strided, dy, xv, rs, w, match=DEVICE_MSG)
+    expect(ValueError, rn.rmsnorm_bwd_strided, act(T, HEADS + 1, H), xv, rs, w, match="dy has shape")
+    expect(ValueError, rn.rmsnorm_bwd_strided, dy, xv, vec(T), w, match="rstd has")
+    expect(ValueError, rn.rmsnorm_bwd_strided, dy, xv, rs, w, dx=act(T, HEADS, H - 8), match="dx has shape")
+    expect(ValueError, rn.rmsnorm_bwd_strided, dy, xv, rs, w, dw=vec(H + 8), match="dw has")
+    expect(TypeError, rn.rmsnorm_bwd_recompute, dy, xv, w, match=DEVICE_MSG)
+    expect(ValueError, rn.rmsnorm_bwd_recompute, act(T, HEADS * H), xv, w, match="dy has shape")
+    expect(ValueError, rn.rmsnorm_bwd_recompute, dy, xv, vec(3), match="w has shape")
+
+
+def test_residual_bwd_checks():
+    dy, h, rs, w = act(), act(), vec(T), vec(H, BF)
+    expect(TypeError, rn.rmsnorm_residual_bwd, dy, h, rs, w, match=DEVICE_MSG)
+    expect(TypeError, rn.rmsnorm_residual_bwd, dy, h, rs, w, dres=act().float(), match="dres must be bfloat16")
+    expect(ValueError, rn.rmsnorm_residual_bwd, dy, h, rs, w, dres=act(T, 2 * H), match="dres has shape")
+    expect(ValueError, rn.rmsnorm_residual_bwd, dy, h, rs, w, dres=act(H, T).t(), match="dres must be contiguous")
+    expect(ValueError, rn.rmsnorm_residual_bwd, dy, h, rs, w, dh=act(T + 1, H), match="dh has shape")
+    expect(ValueError, rn.rmsnorm_residual_bwd, dy, h, vec(1), w, match="rstd has")
+    x3 = act(T, HEADS, H)
+    expect(TypeError, rn.rmsnorm_residual_bwd_strided, x3, x3, vec(T * HEADS), vec(H), match=DEVICE_MSG)
+    expect(ValueError, rn.rmsnorm_residual_bwd_strided, x3, x3, vec(T * HEADS), vec(H),
+           dres=act(T, HEADS, 2 * H), match="dres has shape")
+
+
+# ----------------------------------------------------------- LayerNorm
+
+def test_layernorm_checks():
+    x, g, b = act(), vec(H), vec(H)
+    expect(TypeError, rn.layernorm_fwd, x, g, b, match=DEVICE_MSG)
+    expect(TypeError, rn.layernorm_fwd, x, g, vec(H, BF), match="share one dtype")
+    expect(ValueError, rn.layernorm_fwd, x, g, vec(H + 8), match="beta has shape")
+    expect(ValueError, rn.layernorm_fwd, x, g, b, mean=vec(T + 1), match="mean has")
+    dy, mu, rs = act(), vec(T), vec(T)
+    expect(TypeError, rn.layernorm_bwd, dy, x, mu, rs, g, match=DEVICE_MSG)
+    expect(ValueError, rn.layernorm_bwd, act(H, T).t(), x, mu, rs, g, match="dy must be contiguous")
+    expect(ValueError, rn.layernorm_bwd, dy, x, vec(T - 1), rs, g, match="mean has")
+    expect(ValueError, rn.layernorm_bwd, dy, x, mu, rs, g, dbeta=vec(H - 1), match="dbeta has")
+    expect(ValueError, rn.layernorm_bwd, dy, x, mu, rs, g, dgamma=vec(H + 1), match="dgamma has")

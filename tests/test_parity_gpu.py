@@ -4,8 +4,9 @@ Small shapes span several blocks, ragged rows (H not a multiple of the lane
 count), both weight dtypes, both modes, the small-T column-task route and
 the large-T row route. Full-size cases run each workload the method is
 quoted on, in the same launch configuration the benchmark times, and check
-sampled rows of y/dx element by element, every row's rstd, every column of
-dw, and bit-reproducibility of deterministic dw.
+every element of y and dx (dh, h), every row's rstd, every column of dw, and
+bit-reproducibility of deterministic dw; outputs are filled with a NaN
+pattern first, so an element the kernels never write fails.
 
 The backward is fed the oracle's rstd rounded to FP32 (never the GPU
 forward's), so no oracle input comes from the HIP path.
@@ -18,7 +19,7 @@ import torch
 
 import bwd_rmsnorm_fwd_02_amd as rn
 import oracle
-from tests import synth
+from tests import fullsize, synth
 from tests.parity import (check_bf16_strict, check_dw, check_dx, check_rstd, dx_bound,
                           oracle_rstd32, to_f64)
 
@@ -219,104 +220,112 @@ def test_atomic_route_with_dirty_workspace():
 
 # --------------------------------------------------------- full-size cases
 
-def _sample_rows(rows: int, extra=None, k: int = 48, seed: int = 123) -> np.ndarray:
-    rng = np.random.default_rng(seed)
-    pick = set(rng.choice(rows, min(k, rows), replace=False).tolist())
-    pick.update([0, rows - 1])
-    if extra is not None:
-        pick.update(int(v) for v in extra[:16])
-    return np.array(sorted(pick))
+def filled(shape, device=DEV) -> torch.Tensor:
+    """A BF16 buffer holding the NaN fill pattern in every element."""
+    return torch.full(shape, fullsize.SENTINEL, dtype=torch.int16, device=device).view(torch.bfloat16)
+
+
+def nan_f32(n: int) -> torch.Tensor:
+    return torch.full((n,), float("nan"), dtype=torch.float32, device=DEV)
 
 
 @pytest.mark.parametrize("name", list(synth.CONFIGS) + list(synth.WIDTH_CONFIGS))
 def test_full_size_config(name):
+    """Every element of y, dx (dh) and h of the full-size workload, in the
+    launch configuration the benchmark times, against the oracle; every
+    row's rstd and every column of dw; deterministic dw bit-identical over
+    10 runs; dx identical between the modes. Outputs start as NaN patterns."""
     _announce(f"full-size {name}: generating")
     wl = synth.config(name, seed=0)
     rows, H = wl.rows, wl.H
     w = dev_w(wl.w)
     res = wl.r is not None
+    shape3 = (wl.T, wl.heads, H)
     # ---------------- forward on the GPU
     if res:
-        x_in = wl.x
-        h, y, rstd = rn.rmsnorm_residual_fwd(dev_bf16(wl.x), dev_bf16(wl.r), w, wl.eps)
+        h = filled((rows, H))
+        y = filled((rows, H))
+        h, y, rstd = rn.rmsnorm_residual_fwd(dev_bf16(wl.x), dev_bf16(wl.r), w, wl.eps, h=h, y=y,
+                                             rstd=nan_f32(rows))
         torch.cuda.synchronize()
-        h_ref = oracle.residual_add(wl.x, wl.r)
-        assert np.array_equal(host_bits(h), h_ref), "h not bit-exact"
+        x_in = oracle.residual_add(wl.x, wl.r)
+        assert np.array_equal(host_bits(h), x_in), "h not bit-exact"
         del h
-        x_in = h_ref
     elif wl.xbuf is not None:
         xbuf = dev_bf16(wl.xbuf)
         xd = xbuf[:, : wl.heads * H].unflatten(1, (wl.heads, H))
-        y, rstd = rn.rmsnorm_fwd_strided(xd, w, wl.eps)
+        y, rstd = rn.rmsnorm_fwd_strided(xd, w, wl.eps, y=filled(shape3), rstd=nan_f32(rows))
         x_in = wl.x
     elif wl.heads > 1:
-        xd = dev_bf16(wl.x).view(wl.T, wl.heads, H)
-        y, rstd = rn.rmsnorm_fwd_strided(xd, w, wl.eps)
+        xd = dev_bf16(wl.x).view(shape3)
+        y, rstd = rn.rmsnorm_fwd_strided(xd, w, wl.eps, y=filled(shape3), rstd=nan_f32(rows))
         x_in = wl.x
     else:
         xd = dev_bf16(wl.x)
-        y, rstd = rn.rmsnorm_fwd(xd, w, wl.eps)
+        y, rstd = rn.rmsnorm_fwd(xd, w, wl.eps, y=filled((rows, H)), rstd=nan_f32(rows))
         x_in = wl.x
     torch.cuda.synchronize()
-    _announce(f"full-size {name}: oracle forward over all rows")
+    _announce(f"full-size {name}: oracle forward, all {rows} rows")
     r64, r32 = oracle_rstd32(x_in, wl.w.f64, wl.eps)
     check_rstd("rstd (all rows)", rstd.cpu().numpy().reshape(-1), r64)
-    sample = _sample_rows(rows, wl.heavy_rows)
-    _, y64 = oracle.fwd(x_in[sample], wl.w.f64, wl.eps)
     ybits = host_bits(y).reshape(rows, H)
-    check_bf16_strict("y (sampled rows)", ybits[sample], y64)
-    del y, ybits
+    del y
+    fullsize.check_y_rows("y", ybits, x_in, wl.w.f64, wl.eps)
+    del ybits
     # ---------------- backward on the GPU, fed the oracle's FP32 rstd
     rs = dev_f32(r32)
     dy = dev_bf16(wl.dy)
     r32_64 = r32.astype(np.float64)
-    _announce(f"full-size {name}: oracle dw over all rows")
+    _announce(f"full-size {name}: oracle dw over all rows, both rstd forms")
     _, _, dw64 = oracle.bwd(wl.dy, x_in, r32_64, wl.w.f64, want_dx=False)
     _, _, dw64_i = oracle.bwd(wl.dy, x_in, r64, wl.w.f64, want_dx=False)
-    dx64, c64, _ = oracle.bwd(wl.dy[sample], x_in[sample], r32_64[sample], wl.w.f64)
-    dres64 = to_f64(wl.dres[sample]) if (res and wl.dres is not None) else None
-    E = dx_bound(to_f64(x_in[sample]), to_f64(wl.dy[sample]), wl.w.f64, r32_64[sample], c64, H, dres64)
-    ref_dx = dx64 + (dres64 if dres64 is not None else 0.0)
+    if res:
+        x_dev = dev_bf16(x_in)
+
     def run_bwd(det):
+        dwt = nan_f32(H)
         if res:
-            dx, dw = rn.rmsnorm_residual_bwd(dy, dev_bf16(x_in), rs, w,
+            dx, dw = rn.rmsnorm_residual_bwd(dy, x_dev, rs, w,
                                              dres=dev_bf16(wl.dres) if wl.dres is not None else None,
-                                             deterministic=det)
+                                             deterministic=det, dh=filled((rows, H)), dw=dwt)
             torch.cuda.synchronize()
             return host_bits(dx).reshape(rows, H), dw.cpu().numpy()
         if wl.xbuf is not None:
-            sentinel = 0x7FC0
-            dxbuf = torch.full(wl.xbuf.shape, sentinel, dtype=torch.int16, device=DEV).view(torch.bfloat16)
+            dxbuf = filled(wl.xbuf.shape)
             dxv = dxbuf[:, : wl.heads * H].unflatten(1, (wl.heads, H))
-            _, dw = rn.rmsnorm_bwd_strided(dy.view(wl.T, wl.heads, H), xd, rs.view(wl.T, wl.heads), w,
-                                           deterministic=det, dx=dxv)
+            _, dw = rn.rmsnorm_bwd_strided(dy.view(shape3), xd, rs.view(wl.T, wl.heads), w,
+                                           deterministic=det, dx=dxv, dw=dwt)
             torch.cuda.synchronize()
             full = host_bits(dxbuf)
-            assert np.all(full[:, wl.heads * H:] == sentinel), "gap columns written"
+            assert np.all(full[:, wl.heads * H:] == fullsize.SENTINEL), "gap columns written"
             return np.ascontiguousarray(full[:, : wl.heads * H]).reshape(rows, H), dw.cpu().numpy()
         if wl.heads > 1:
-            dx, dw = rn.rmsnorm_bwd_strided(dy.view(wl.T, wl.heads, H), xd, rs.view(wl.T, wl.heads), w,
-                                            deterministic=det)
+            dx, dw = rn.rmsnorm_bwd_strided(dy.view(shape3), xd, rs.view(wl.T, wl.heads), w,
+                                            deterministic=det, dx=filled(shape3), dw=dwt)
             torch.cuda.synchronize()
             return host_bits(dx).reshape(rows, H), dw.cpu().numpy()
-        dx, dw = rn.rmsnorm_bwd(dy, xd, rs, w, deterministic=det)
+        dx, dw = rn.rmsnorm_bwd(dy, xd, rs, w, deterministic=det, dx=filled((rows, H)), dw=dwt)
         torch.cuda.synchronize()
         return host_bits(dx), dw.cpu().numpy()
 
-    dx_bits = {}
+    det_dx_bits = None
     det_dw_bits = None
     for det in (True, False):
         _announce(f"full-size {name}: backward det={det}")
         dxb, dwn = run_bwd(det)
-        n_ex = check_dx(f"dx det={det} (sampled rows)", dxb[sample], ref_dx, E)
         f2 = check_dw(f"dw det={det} (forward's rstd)", dwn, dw64)
         f1 = check_dw(f"dw det={det} (FP64 rstd)", dwn, dw64_i)
-        _announce(f"  dx exempted={n_ex} dw worst/budget={f2:.4f} (fp64-rstd form {f1:.4f})")
-        dx_bits[det] = dxb[sample].copy()
         if det:
-            det_dw_bits = dwn.view(np.uint32).copy()
+            n_ex = fullsize.check_dx_rows("dx det", dxb, wl.dy, x_in, r32_64, wl.w.f64,
+                                          wl.dres if res else None)
+            _announce(f"  dx all rows: exempted={n_ex}; dw worst/budget={f2:.4f} "
+                      f"(fp64-rstd form {f1:.4f})")
+            det_dx_bits, det_dw_bits = dxb, dwn.view(np.uint32).copy()
+        else:
+            assert np.array_equal(dxb, det_dx_bits), "dx differs between modes"
+            _announce(f"  non-det: dx identical to det; dw worst/budget={f2:.4f} ({f1:.4f})")
         del dxb
-    assert np.array_equal(dx_bits[True], dx_bits[False]), "dx differs between modes"
+    del det_dx_bits
     # deterministic dw: bit-identical over 10 runs
     for i in range(10):
         _, dwn = run_bwd(True)
@@ -383,6 +392,172 @@ def test_route_variants(T, H, wdt, op, knobs):
             assert np.array_equal(outs[0][0], dx_det)
     finally:
         rn.rmsnorm_route_override(op)
+
+
+# ------------------------------------------- load policies at small shapes
+#
+# The non-temporal load variants (stream_loads level 1: dy and dres streamed;
+# level 2: every input streamed, and the residual forward's x and r) run by
+# default only at sizes where the full-size cases check them. Here every form
+# is forced onto each level at small shapes, ragged and multi-block, and
+# compared element by element; the route knob takes 1 + the level.
+
+LOAD_POLICY_CASES = [
+    # (form, T, heads, H, w dtype)
+    ("fwd", 777, 1, 2048, "f32"),
+    ("res_fwd", 333, 1, 6144, "bf16"),
+    ("res_fwd", 1001, 1, 256, "f32"),
+    ("bwd", 777, 1, 2048, "f32"),
+    ("bwd", 3001, 1, 256, "bf16"),
+    ("bwd", 129, 1, 16384, "bf16"),
+    ("res_bwd", 333, 1, 6144, "bf16"),
+    ("res_bwd_nodres", 333, 1, 6144, "f32"),
+    ("strided_bwd", 300, 24, 256, "f32"),
+]
+
+
+def _check_form(form, wl, det=True):
+    """Run `form` on the GPU for workload wl and check it against the oracle
+    (all elements). Returns the output bits for cross-checks."""
+    H, rows = wl.H, wl.rows
+    w = dev_w(wl.w)
+    if form in ("fwd", "res_fwd"):
+        if form == "res_fwd":
+            h, y, rstd = rn.rmsnorm_residual_fwd(dev_bf16(wl.x), dev_bf16(wl.r), w, wl.eps,
+                                                 h=filled((rows, H)), y=filled((rows, H)))
+            torch.cuda.synchronize()
+            x_in = oracle.residual_add(wl.x, wl.r)
+            assert np.array_equal(host_bits(h), x_in), "h not bit-exact"
+        else:
+            y, rstd = rn.rmsnorm_fwd(dev_bf16(wl.x), w, wl.eps, y=filled((rows, H)))
+            torch.cuda.synchronize()
+            x_in = wl.x
+        r64, y64 = oracle.fwd(x_in, wl.w.f64, wl.eps)
+        check_rstd("rstd", rstd.cpu().numpy(), r64)
+        yb = host_bits(y)
+        check_bf16_strict("y", yb, y64)
+        return yb
+    x_in = oracle.residual_add(wl.x, wl.r) if wl.r is not None else wl.x
+    _, r32 = oracle_rstd32(x_in, wl.w.f64, wl.eps)
+    r32_64 = r32.astype(np.float64)
+    _, _, dw64 = oracle.bwd(wl.dy, x_in, r32_64, wl.w.f64, want_dx=False)
+    dres = wl.dres if form == "res_bwd" else None
+    if form in ("res_bwd", "res_bwd_nodres"):
+        dx, dw = rn.rmsnorm_residual_bwd(dev_bf16(wl.dy), dev_bf16(x_in), dev_f32(r32), w,
+                                         dres=dev_bf16(dres) if dres is not None else None,
+                                         deterministic=det, dh=filled((rows, H)))
+        torch.cuda.synchronize()
+        dxb = host_bits(dx)
+    elif form == "strided_bwd":
+        row = 8192
+        xbuf = dev_bf16(wl.xbuf)
+        xv = xbuf[:, : wl.heads * H].unflatten(1, (wl.heads, H))
+        dxbuf = filled((wl.T, row))
+        dxv = dxbuf[:, : wl.heads * H].unflatten(1, (wl.heads, H))
+        _, dw = rn.rmsnorm_bwd_strided(dev_bf16(wl.dy).view(wl.T, wl.heads, H), xv,
+                                       dev_f32(r32).view(wl.T, wl.heads), w, deterministic=det,
+                                       dx=dxv)
+        torch.cuda.synchronize()
+        full = host_bits(dxbuf)
+        assert np.all(full[:, wl.heads * H:] == fullsize.SENTINEL), "gap columns written"
+        dxb = np.ascontiguousarray(full[:, : wl.heads * H]).reshape(rows, H)
+    else:
+        dx, dw = rn.rmsnorm_bwd(dev_bf16(wl.dy), dev_bf16(x_in), dev_f32(r32), w,
+                                deterministic=det, dx=filled((rows, H)))
+        torch.cuda.synchronize()
+        dxb = host_bits(dx)
+    fullsize.check_dx_rows("dx", dxb, wl.dy, x_in, r32_64, wl.w.f64, dres)
+    check_dw("dw", dw.cpu().numpy(), dw64)
+    return dxb
+
+
+@pytest.mark.parametrize("level", [0, 1, 2])
+@pytest.mark.parametrize("form,T,heads,H,wdt", LOAD_POLICY_CASES)
+def test_load_policy_variants(form, T, heads, H, wdt, level):
+    _announce(f"load policy {form} level={level} T={T} heads={heads} H={H} w={wdt}")
+    residual = form.startswith("res")
+    wl = synth.make(T=T, H=H, w_dtype=wdt, seed=T + H + level, heads=heads, residual=residual,
+                    with_dres=(form != "res_bwd_nodres"),
+                    strided_row=8192 if form == "strided_bwd" else 0)
+    op = "fwd" if form.endswith("fwd") else "bwd"
+    try:
+        rn.rmsnorm_route_override(op, stream_loads=level + 1)
+        got = rn.rmsnorm_route_query(op, wl.rows, H, torch.float32 if wdt == "f32" else torch.bfloat16,
+                                     residual=residual)
+        assert got["stream_loads"] == level
+        out = _check_form(form, wl)
+    finally:
+        rn.rmsnorm_route_override(op)
+    # the load policy changes no arithmetic: same bits as the default route
+    assert np.array_equal(_check_form(form, wl), out), "load policy changed the result"
+
+
+@pytest.mark.parametrize("T,heads,H,wdt,with_dres", [(300, 24, 256, "f32", True),
+                                                     (50, 4, 256, "bf16", False),
+                                                     (40, 2, 6144, "bf16", True)])
+def test_residual_views(T, heads, H, wdt, with_dres):
+    """The residual form over per-head views: x, r, h, y, dy, dres and dh each
+    strided inside wider buffers whose gap columns must stay untouched;
+    against the oracle, and bit-identical to the contiguous residual calls."""
+    _announce(f"residual views T={T} heads={heads} H={H} w={wdt} dres={with_dres}")
+    wl = synth.make(T=T, H=H, w_dtype=wdt, seed=T + heads, heads=heads, residual=True,
+                    with_dres=with_dres)
+    rows = wl.rows
+    W = heads * H + 64  # row stride of every wide buffer
+
+    def wide(bits, fill=None):
+        buf = filled((T, W)) if fill else dev_bf16(np.zeros((T, W), np.uint16))
+        if bits is not None:
+            buf[:, : heads * H] = dev_bf16(bits).view(T, heads * H)
+        return buf, buf[:, : heads * H].unflatten(1, (heads, H))
+
+    w = dev_w(wl.w)
+    xb, xv = wide(wl.x)
+    rb, rv = wide(wl.r)
+    hb, hv = wide(None, fill=True)
+    yb, yv = wide(None, fill=True)
+    _, _, rstd = rn.rmsnorm_residual_fwd_strided(xv, rv, w, wl.eps, h=hv, y=yv)
+    torch.cuda.synchronize()
+    h_ref = oracle.residual_add(wl.x, wl.r)
+    for name, b in (("h", hb), ("y", yb)):
+        gap = host_bits(b)[:, heads * H:]
+        assert np.all(gap == fullsize.SENTINEL), f"gap columns of {name} written"
+    hbits = np.ascontiguousarray(host_bits(hb)[:, : heads * H]).reshape(rows, H)
+    assert np.array_equal(hbits, h_ref), "h not bit-exact"
+    r64, y64 = oracle.fwd(h_ref, wl.w.f64, wl.eps)
+    check_rstd("rstd", rstd.cpu().numpy().reshape(-1), r64)
+    ybits = np.ascontiguousarray(host_bits(yb)[:, : heads * H]).reshape(rows, H)
+    check_bf16_strict("y", ybits, y64)
+    # contiguous residual forward on the same rows: same bits
+    hc, yc, rc = rn.rmsnorm_residual_fwd(dev_bf16(wl.x), dev_bf16(wl.r), w, wl.eps)
+    torch.cuda.synchronize()
+    assert np.array_equal(host_bits(hc), hbits) and np.array_equal(host_bits(yc), ybits)
+    assert torch.equal(rc, rstd.reshape(-1))
+    # backward over views, fed the oracle's rstd
+    r32 = oracle.round_f32(r64)
+    r32_64 = r32.astype(np.float64)
+    _, _, dw64 = oracle.bwd(wl.dy, h_ref, r32_64, wl.w.f64, want_dx=False)
+    dyb, dyv = wide(wl.dy)
+    drb, drv = wide(wl.dres) if with_dres else (None, None)
+    hb2, hv2 = wide(h_ref)
+    for det in (True, False):
+        dhb, dhv = wide(None, fill=True)
+        _, dw = rn.rmsnorm_residual_bwd_strided(dyv, hv2, dev_f32(r32).view(T, heads), w, dres=drv,
+                                                deterministic=det, dh=dhv)
+        torch.cuda.synchronize()
+        full = host_bits(dhb)
+        assert np.all(full[:, heads * H:] == fullsize.SENTINEL), "gap columns of dh written"
+        dhbits = np.ascontiguousarray(full[:, : heads * H]).reshape(rows, H)
+        fullsize.check_dx_rows(f"dh det={det}", dhbits, wl.dy, h_ref, r32_64, wl.w.f64,
+                               wl.dres if with_dres else None)
+        check_dw(f"dw det={det}", dw.cpu().numpy(), dw64)
+        dhc, dwc = rn.rmsnorm_residual_bwd(dev_bf16(wl.dy), dev_bf16(h_ref), dev_f32(r32), w,
+                                           dres=dev_bf16(wl.dres) if with_dres else None,
+                                           deterministic=det)
+        torch.cuda.synchronize()
+        assert np.array_equal(host_bits(dhc), dhbits), "views changed dh"
+        if det:
+            assert torch.equal(dwc.view(torch.int32), dw.view(torch.int32)), "views changed dw"
 
 
 # ------------------------------------------------------ non-finite inputs
