@@ -37,8 +37,9 @@ Timing (the pages' protocol, Cake page "Measurement", on HIP graphs):
   value = algorithmic bytes of one step / ms_per_step;
 * before each round, one untimed replay of each deterministic graph is
   checked bit for bit against the eager result;
-* roofline: the same K steps launched eagerly, each library kernel bracketed
-  by HIP events recorded on its launch stream by the dispatch itself; the
+* roofline: the same steps launched eagerly (max(40, K) timed after
+  max(10, K) untimed), each library kernel bracketed by HIP events recorded
+  on its launch stream by the dispatch itself; the
   dominant kernel is the backward row kernel (the forward for --op fwd);
   achieved = its algorithmic bytes per launch / its mean duration; peak
   8 TB/s. frac_cold is the same kernel timed in backward-only steps (no
@@ -355,16 +356,22 @@ def measure_op(args, torch, rn, _lib, dev, wk, op, nondet=True):
     st = {k: stats(v) for k, v in spans.items()}
     aa = abs(1.0 - st["det"]["median"] / st["det_aa"]["median"])
 
-    # Per-kernel HIP-event timing of the same K steps, launched eagerly. The
-    # GPU is first parked on a sleep kernel so that the host queues all K
-    # steps before any runs: the kernels then run back to back and each
-    # event pair brackets GPU time only, not host launch gaps.
+    # Per-kernel HIP-event timing of the same steps, launched eagerly. The
+    # GPU is first parked on a sleep kernel so that the host queues every
+    # step before any runs: the kernels then run back to back and each event
+    # pair brackets GPU time only, not host launch gaps. The first K_WARM
+    # queued steps are not timed: the kernels right after the idle sleep run
+    # slower while the part ramps back up.
+    k_warm, k_timed = max(10, K), max(40, K)
     rn.rmsnorm_timing_read()
-    rn.rmsnorm_timing_enable(True)
+    rn.rmsnorm_timing_enable(False)
     torch.cuda.synchronize()
     torch.cuda._sleep(int(2e8))
     t0 = time.perf_counter()
-    for i in range(K):
+    for i in range(k_warm):
+        step(sets[i % n_sets], 1, sp)
+    rn.rmsnorm_timing_enable(True)
+    for i in range(k_warm, k_warm + k_timed):
         step(sets[i % n_sets], 1, sp)
     t_issue = time.perf_counter() - t0
     torch.cuda.synchronize()
@@ -380,7 +387,8 @@ def measure_op(args, torch, rn, _lib, dev, wk, op, nondet=True):
     sb = wk.step_bytes(op)
     ms = st["det"]["median"]
     return {"op": op, "step_bytes": sb, "ms_per_step": ms, "stats": st, "aa_noise": aa,
-            "value": gbps(sb, ms), "kernel_us": ku, "t_issue_ms": t_issue * 1e3 / K, "K": K, "W": W}
+            "value": gbps(sb, ms), "kernel_us": ku, "t_issue_ms": t_issue * 1e3 / (k_warm + k_timed),
+            "K": K, "W": W, "kernel_steps": k_timed}
 
 
 def dominant(wk, op, m):
