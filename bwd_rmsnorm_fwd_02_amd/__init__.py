@@ -23,7 +23,7 @@ from ._lib import RMSNormError, View  # noqa: F401
 __all__ = [
     "rmsnorm_fwd", "rmsnorm_fwd_strided", "rmsnorm_residual_fwd", "rmsnorm_residual_fwd_strided",
     "rmsnorm_bwd", "rmsnorm_bwd_strided", "rmsnorm_bwd_recompute", "rmsnorm_residual_bwd",
-    "rmsnorm_residual_bwd_strided", "layernorm_fwd", "layernorm_bwd",
+    "rmsnorm_residual_bwd_strided", "rmsnorm_bwd_strided_noalloc", "layernorm_fwd", "layernorm_bwd",
     "layernorm_bwd_workspace_bytes", "rmsnorm_bwd_workspace_bytes",
     "rmsnorm_workspace_init", "rmsnorm_status_string", "rmsnorm_route_query",
     "rmsnorm_route_override", "rmsnorm_timing_enable", "rmsnorm_timing_read",
@@ -328,6 +328,29 @@ def rmsnorm_bwd_strided(dy: torch.Tensor, x: torch.Tensor, rstd: torch.Tensor, w
                                                _ptr(w), wd, int(bool(deterministic)),
                                                _ptr(dx), dxv, _ptr(dw), _ptr(ws), nbytes,
                                                _stream(dev)))
+    return dx, dw
+
+
+def rmsnorm_bwd_strided_noalloc(dy: torch.Tensor, x: torch.Tensor, rstd: torch.Tensor,
+                                w: torch.Tensor, deterministic: bool = True,
+                                dx: Optional[torch.Tensor] = None,
+                                dw: Optional[torch.Tensor] = None):
+    """rmsnorm_bwd_strided with the library's fixed scratch as workspace (no
+    allocation by the library; calls on one device must not overlap). Pass
+    dx and dw to allocate nothing here either."""
+    _need_bf16("x", x)
+    dev = x.device
+    xv = _view(x)
+    rows = xv.T * xv.heads
+    dyv = _need_view("dy", dy, dev, x.shape)
+    _need_f32("rstd", rstd, dev, rows)
+    wd = _need_weight("w", w, dev, xv.H)
+    dx, dw = _bwd_outputs(dev, x.shape, xv.H, dx, dw)
+    dxv = _need_view("dx", dx, dev, x.shape)
+    _need_gpu(dev)
+    _lib.check(_lib.load().rmsnorm_bwd_strided_noalloc(_ptr(dy), dyv, _ptr(x), xv, _ptr(rstd),
+                                                       _ptr(w), wd, int(bool(deterministic)),
+                                                       _ptr(dx), dxv, _ptr(dw), _stream(dev)))
     return dx, dw
 
 

@@ -32,7 +32,7 @@ RMSN_TIMER_COUNT = 8
 STATUS = {
     0: "RMSN_OK", -1: "RMSN_ERR_NULL", -2: "RMSN_ERR_DTYPE", -3: "RMSN_ERR_SHAPE",
     -4: "RMSN_ERR_ALIGN", -5: "RMSN_ERR_WORKSPACE", -6: "RMSN_ERR_OVERFLOW",
-    -7: "RMSN_ERR_ALIAS", -8: "RMSN_ERR_LAUNCH", -9: "RMSN_ERR_EPS",
+    -7: "RMSN_ERR_ALIAS", -8: "RMSN_ERR_LAUNCH", -9: "RMSN_ERR_EPS", -10: "RMSN_ERR_SCRATCH",
 }
 
 # Every symbol include/rmsnorm.h declares.
@@ -40,7 +40,7 @@ EXPORTS = [
     "rmsnorm_fwd", "rmsnorm_fwd_strided", "rmsnorm_residual_fwd", "rmsnorm_residual_fwd_strided",
     "rmsnorm_bwd_workspace_bytes", "rmsnorm_workspace_init", "rmsnorm_bwd",
     "rmsnorm_bwd_strided", "rmsnorm_bwd_recompute", "rmsnorm_residual_bwd",
-    "rmsnorm_residual_bwd_strided",
+    "rmsnorm_residual_bwd_strided", "rmsnorm_bwd_strided_noalloc",
     "rmsnorm_status_string",
     "rmsnorm_route_query", "rmsnorm_route_override", "rmsnorm_timing_enable",
     "rmsnorm_timing_read", "layernorm_fwd", "layernorm_bwd_workspace_bytes", "layernorm_bwd",
@@ -112,6 +112,7 @@ def load() -> ctypes.CDLL:
         "rmsnorm_workspace_init": [p, sz, p],
         "rmsnorm_bwd": [p, p, p, p, i32, i32, p, p, i64, i64, p, sz, p],
         "rmsnorm_bwd_strided": [p, View, p, View, p, p, i32, i32, p, View, p, p, sz, p],
+        "rmsnorm_bwd_strided_noalloc": [p, View, p, View, p, p, i32, i32, p, View, p, p],
         "rmsnorm_bwd_recompute": [p, View, p, View, p, i32, f32, i32, p, View, p, p, sz, p],
         "rmsnorm_residual_bwd": [p, p, p, p, p, i32, i32, p, p, i64, i64, p, sz, p],
         "rmsnorm_residual_bwd_strided": [p, View, p, View, p, View, p, p, i32, i32, p, View, p, p,

@@ -16,7 +16,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libbwd_rmsnorm.so")
 SOURCES = ["fwd_bf16w.hip", "fwd_f32w.hip", "bwd_bf16w.hip", "bwd_f32w.hip", "ln_bf16w.hip",
-           "ln_f32w.hip", "reduce.hip", "route.cpp", "api.cpp"]
+           "ln_f32w.hip", "reduce.hip", "route.cpp", "api.cpp", "noalloc.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # Packed FP32 vector instructions are disabled for every HIP source (the

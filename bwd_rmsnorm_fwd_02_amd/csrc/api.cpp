@@ -578,6 +578,9 @@ const char* rmsnorm_status_string(int status) {
                    "forward is allowed) or an output view's rows overlap each other";
         case RMSN_ERR_LAUNCH: return "a HIP kernel launch failed";
         case RMSN_ERR_EPS: return "eps must be finite and >= 0";
+        case RMSN_ERR_SCRATCH:
+            return "the problem needs more dw partial rows than the no-alloc entry point's fixed "
+                   "32 MiB scratch holds (or its device address could not be looked up)";
         default: return "unknown status";
     }
 }

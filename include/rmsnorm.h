@@ -78,7 +78,9 @@ enum {
     RMSN_ERR_OVERFLOW = -6,  /* element offsets or byte sizes overflow int64 */
     RMSN_ERR_ALIAS = -7,     /* an output overlaps another tensor (not exact in-place) */
     RMSN_ERR_LAUNCH = -8,    /* a kernel launch failed (hipGetLastError) */
-    RMSN_ERR_EPS = -9        /* eps negative, NaN or infinite */
+    RMSN_ERR_EPS = -9,       /* eps negative, NaN or infinite */
+    RMSN_ERR_SCRATCH = -10   /* the no-alloc entry point's fixed scratch is too small
+                                (or its address could not be looked up) */
 };
 
 typedef struct {
@@ -158,6 +160,21 @@ int rmsnorm_bwd_strided(const void* dy, rmsn_view_t dyv, const void* x, rmsn_vie
                         const float* rstd, const void* w, rmsn_dtype_t w_dtype,
                         int deterministic, void* dx, rmsn_view_t dxv, float* dw,
                         void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* For callers that cannot allocate (code under graph capture, tight
+ * serving loops, harnesses that forbid allocation): rmsnorm_bwd_strided
+ * with no workspace argument. The dw partial rows go to a fixed device array
+ * of 32 MiB inside the library, enough for every shape at the default
+ * routes; a problem needing more returns RMSN_ERR_SCRATCH before anything is
+ * enqueued. Each device holds its own array until the process ends. All
+ * calls on one device share that array, so calls that may overlap on one
+ * device (other streams, other host threads) race and must be serialised
+ * by the caller. Everything else as rmsnorm_bwd_strided; the results are
+ * bit-identical to it. Makes no allocation. */
+int rmsnorm_bwd_strided_noalloc(const void* dy, rmsn_view_t dyv, const void* x, rmsn_view_t xv,
+                                const float* rstd, const void* w, rmsn_dtype_t w_dtype,
+                                int deterministic, void* dx, rmsn_view_t dxv, float* dw,
+                                hipStream_t stream);
 
 /* Backward that takes no rstd: each row's rstd is recomputed from x inside
  * the backward kernel, while the row is in registers, with the forward's own

@@ -40,7 +40,7 @@ def test_header_declarations_are_exported():
 
 
 def test_status_strings():
-    for code in range(-9, 1):
+    for code in range(-10, 1):
         s = _lib.status_string(code)
         assert s and s != "unknown status", code
     assert _lib.status_string(-100) == "unknown status"

@@ -1,0 +1,100 @@
+"""rmsnorm_bwd_strided_noalloc, the backward for callers that cannot
+allocate, through the C ABI: its dx and dw are bit-identical to
+rmsnorm_bwd_strided's (same kernels, same partition) on two calls in a row,
+the second smaller than the first, in both modes, and within the oracle's
+budgets; a problem needing more than its fixed scratch is refused before
+anything is enqueued. The library's scratch keeps the last call's contents,
+so the second call also shows that nothing depends on it starting clean."""
+from __future__ import annotations
+
+import ctypes
+
+import numpy as np
+import pytest
+import torch
+
+import bwd_rmsnorm_fwd_02_amd as rn
+import oracle
+from bwd_rmsnorm_fwd_02_amd import _lib
+from tests import fullsize, synth
+from tests.parity import check_dw, oracle_rstd32
+from tests.test_parity_gpu import DEV, _announce, dev_bf16, dev_f32, dev_w, filled, host_bits, nan_f32
+
+pytestmark = pytest.mark.gpu
+
+P = ctypes.c_void_p
+
+
+def _views(T, heads, H):
+    c = _lib.View(T, heads, H, heads * H, H)
+    return c
+
+
+def _run(lib, fn_name, wl, det, ws=None):
+    T, heads, H = wl.T, wl.heads, wl.H
+    v = _views(T, heads, H)
+    x, dy, w = dev_bf16(wl.x), dev_bf16(wl.dy), dev_w(wl.w)
+    _, r32 = oracle_rstd32(wl.x, wl.w.f64, wl.eps)
+    rs = dev_f32(r32)
+    dx = filled((wl.rows, H))
+    dw = nan_f32(H)
+    wdt = _lib.RMSN_BF16 if wl.w.dtype == "bf16" else _lib.RMSN_F32
+    s = P(torch.cuda.current_stream().cuda_stream)
+    if fn_name == "noalloc":
+        st = lib.rmsnorm_bwd_strided_noalloc(P(dy.data_ptr()), v, P(x.data_ptr()), v, P(rs.data_ptr()),
+                                             P(w.data_ptr()), wdt, int(det), P(dx.data_ptr()), v,
+                                             P(dw.data_ptr()), s)
+    else:
+        st = lib.rmsnorm_bwd_strided(P(dy.data_ptr()), v, P(x.data_ptr()), v, P(rs.data_ptr()),
+                                     P(w.data_ptr()), wdt, int(det), P(dx.data_ptr()), v,
+                                     P(dw.data_ptr()), P(ws.data_ptr()), ws.numel(), s)
+    _lib.check(st)
+    torch.cuda.synchronize()
+    return host_bits(dx), dw.cpu().numpy(), r32
+
+
+def test_noalloc_matches_the_workspace_entry_point():
+    lib = _lib.load()
+    # first call large (FP64 partial rows, several MB of scratch), second
+    # smaller (FP32 partial rows) over the first call's leftovers
+    cases = [dict(T=16384, H=4096, w_dtype="bf16", seed=41),
+             dict(T=3000, heads=4, H=256, w_dtype="f32", seed=42)]
+    for det in (True, False):
+        for kw in cases:
+            wl = synth.make(**kw)
+            _announce(f"no-alloc det={det} T={wl.T} heads={wl.heads} H={wl.H}")
+            need = rn.rmsnorm_bwd_workspace_bytes(wl.rows, wl.H, torch.bfloat16 if wl.w.dtype == "bf16"
+                                                  else torch.float32, det)
+            raw = torch.empty(need + 256, dtype=torch.uint8, device=DEV)
+            ws = raw[(-raw.data_ptr()) % 256:]
+            dx_n, dw_n, r32 = _run(lib, "noalloc", wl, det)
+            dx_w, dw_w, _ = _run(lib, "workspace", wl, det, ws)
+            assert np.array_equal(dx_n, dx_w), "dx differs from rmsnorm_bwd_strided"
+            assert np.array_equal(dw_n.view(np.uint32), dw_w.view(np.uint32)), \
+                "dw differs from rmsnorm_bwd_strided"
+            _, _, dw64 = oracle.bwd(wl.dy, wl.x, r32.astype(np.float64), wl.w.f64, want_dx=False)
+            check_dw("dw (no-alloc)", dw_n, dw64)
+            fullsize.check_dx_rows("dx (no-alloc)", dx_n, wl.dy, wl.x, r32.astype(np.float64), wl.w.f64)
+
+
+def test_noalloc_refuses_more_than_its_scratch():
+    """A tuning override that quadruples the row blocks at H 8192 asks for 64 MiB
+    of FP64 partial rows: refused on the host, nothing launched."""
+    lib = _lib.load()
+    T, H = 65536, 8192
+    try:
+        rn.rmsnorm_route_override("bwd", blocks_per_cu=4)
+        r = rn.rmsnorm_route_query("bwd", T, H, torch.bfloat16)
+        assert r["partials"] * H * 8 > (32 << 20)
+        x = torch.zeros(T, H, dtype=torch.bfloat16, device=DEV)
+        rs = torch.ones(T, dtype=torch.float32, device=DEV)
+        w = torch.ones(H, dtype=torch.bfloat16, device=DEV)
+        dw = torch.zeros(H, dtype=torch.float32, device=DEV)
+        v = _views(T, 1, H)
+        s = P(torch.cuda.current_stream().cuda_stream)
+        st = lib.rmsnorm_bwd_strided_noalloc(P(x.data_ptr()), v, P(x.data_ptr()), v, P(rs.data_ptr()),
+                                             P(w.data_ptr()), _lib.RMSN_BF16, 1, P(x.data_ptr() + 0),
+                                             v, P(dw.data_ptr()), s)
+        assert st == -10, st
+    finally:
+        rn.rmsnorm_route_override("bwd")
