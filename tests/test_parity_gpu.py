@@ -63,6 +63,9 @@ SMALL = [
     # widths between 2048 and 4096: three row groups of 320 lanes per block
     # up to H 2560, two of 384 or 448 lanes above
     (333, 2304, "bf16"), (1001, 2560, "f32"), (97, 3072, "bf16"), (129, 3584, "f32"),
+    # more small-T column-task shapes: ragged widths, a single column chunk,
+    # narrow rows, and T just below the row route
+    (17, 136, "bf16"), (32, 512, "f32"), (33, 512, "bf16"), (64, 8, "f32"), (2, 520, "f32"),
 ]
 
 
@@ -108,7 +111,8 @@ def test_bwd_small(T, H, wdt):
 
 
 @pytest.mark.parametrize("T,H,wdt,with_dres", [(64, 6144, "bf16", True), (333, 6144, "bf16", True),
-                                                (333, 6144, "f32", False), (100, 256, "f32", True)])
+                                                (333, 6144, "f32", False), (100, 256, "f32", True),
+                                                (50, 256, "f32", True), (7, 512, "bf16", False)])
 def test_residual_small(T, H, wdt, with_dres):
     _announce(f"residual T={T} H={H} w={wdt} dres={with_dres}")
     wl = synth.make(T=T, H=H, w_dtype=wdt, seed=T + 7, residual=True, with_dres=with_dres)
