@@ -510,6 +510,9 @@ def main() -> int:
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-per-config", action="store_true",
                     help="time only the chosen workload, not every workload of its family")
+    ap.add_argument("--no-cold", action="store_true",
+                    help="skip the backward-only (cold) timing of the chosen workload, so that "
+                         "a kernel trace holds the in-step launches of its kernels only")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="seconds of oracle work for each of the two CPU runs")
     ap.add_argument("--cpu-threads", type=int, default=0,
@@ -569,7 +572,7 @@ def main() -> int:
     progress(f"{args.config} {op}: timing")
     m = measure_op(args, torch, rn, _lib, dev, wk, op)
     cold = None
-    if op != "fwd" and op != "bwd":
+    if op != "fwd" and op != "bwd" and not args.no_cold:
         progress(f"{args.config} bwd alone: timing (cold backward)")
         cold = measure_op(args, torch, rn, _lib, dev, wk, "bwd", nondet=False)
     dom_name, dom_bytes, dom_us = dominant(wk, op, m)
