@@ -44,8 +44,9 @@ Timing (the pages' protocol, Cake page "Measurement", on HIP graphs):
   achieved = its algorithmic bytes per launch / its mean duration; peak
   8 TB/s. frac_cold is the same kernel timed in backward-only steps (no
   forward before it, so nothing of x is left in the caches);
-* per_config: fwd, bwd and fwd+bwd of every workload of the family, with the
-  same protocol, in the same run (--no-per-config skips it);
+* per_config: fwd, bwd, fwd+bwd and 2xfwd+bwd (the pages' three timed ops
+  and the metric's step) of every workload of the family, with the same
+  protocol, in the same run (--no-per-config skips it);
 * cpu_baseline: the FP64 oracle on the same work, called on row slices from
   a pool of host threads (the oracle's C code runs without the interpreter
   lock), and single-threaded beside it.
@@ -608,7 +609,7 @@ def main() -> int:
             progress(f"per-config {name}: generating inputs")
             w2 = prepare(name, args.seed, torch, np, synth, _lib, lib, dev)
             entry = per_config.setdefault(name, {})
-            for o in ("fwd+bwd", "bwd", "fwd"):
+            for o in ("fwd+bwd", "bwd", "fwd", "2xfwd+bwd"):
                 if o in entry:
                     continue
                 progress(f"per-config {name} {o}: timing")

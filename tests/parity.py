@@ -2,10 +2,11 @@
 
 Budgets (flashinfer PR "fix(cake_rmsnorm): sm_100a and sm_107a dw-accuracy
 backward routes"):
-* dw: per element |dw - dw64| <= 1e-4 + 1e-4 |dw64| ("Changed windows by
-  reason": "per element atol 1e-4 + rtol 1e-4 vs FP64"), checked against the
-  FP64 sum at the forward's FP32 rstd and at the FP64-recomputed rstd (the
-  pages' "both rstd forms");
+* dw: per element |dw - dw64| <= 1e-4 + 1e-4 |dw64| (the dw budget of
+  "Changed windows by reason": absolute and relative tolerance 1e-4 on each
+  element against FP64), checked against the oracle's sum taken at the FP32
+  rstd the backward is given and against its sum at the rstd recomputed in
+  FP64 (the page's two rstd forms);
 * y and dx: within one BF16 ulp of the FP64 value rounded to BF16. y is
   checked strictly. dx = rstd*(g - xhat*c) can cancel, and no FP32 evaluation
   can promise one ulp there: an element whose FP32 evaluation bound E exceeds

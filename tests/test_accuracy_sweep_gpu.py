@@ -3,11 +3,11 @@ dw-accuracy backward routes", section "Changed windows by reason", and the
 "Tests" list of the re-vendoring commit on the same page).
 
 The page qualifies a route by sampling every 64th token count of a window
-(and both sides of each edge) with 60, 120 or 240 inputs of each of three
-input families, at both rstd forms, against the dw budget and against the
-FP32 eager computation: a program fails the latter if its largest dw error
-is above the eager one's (FP32 weight) or its median dw error is above the
-eager median (either weight dtype). Here the eager computation is torch in
+(and both sides of each edge) with 60, 120 or 240 inputs per input family
+(three families), at both rstd forms, against the dw budget and against the
+FP32 eager computation. Against the latter, a route must not have a larger
+worst-case dw error than the eager result with an FP32 weight, nor a larger
+median dw error with either weight dtype. Here the eager computation is torch in
 float32 on the GPU, dw = sum over t of dy * (x * rstd), at the same FP32
 rstd, and its error is measured against the same FP64 dw.
 
