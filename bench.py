@@ -37,9 +37,9 @@ Timing (the pages' protocol, Cake page "Measurement", on HIP graphs):
   value = algorithmic bytes of one step / ms_per_step;
 * before each round, one untimed replay of each deterministic graph is
   checked bit for bit against the eager result;
-* roofline: the same steps launched eagerly (max(40, K) timed after
-  max(10, K) untimed), each library kernel bracketed by HIP events recorded
-  on its launch stream by the dispatch itself; the
+* roofline: the same steps launched eagerly (max(40, K) timed after about
+  25 ms of untimed ones), each library kernel bracketed by HIP events
+  recorded on its launch stream by the dispatch itself; the
   dominant kernel is the backward row kernel (the forward for --op fwd);
   achieved = its algorithmic bytes per launch / its mean duration; peak
   8 TB/s. frac_cold is the same kernel timed in backward-only steps (no
@@ -358,12 +358,15 @@ def measure_op(args, torch, rn, _lib, dev, wk, op, nondet=True):
     aa = abs(1.0 - st["det"]["median"] / st["det_aa"]["median"])
 
     # Per-kernel HIP-event timing of the same steps, launched eagerly. The
-    # GPU is first parked on a sleep kernel so that the host queues every
-    # step before any runs: the kernels then run back to back and each event
-    # pair brackets GPU time only, not host launch gaps. The first K_WARM
-    # queued steps are not timed: the kernels right after the idle sleep run
-    # slower while the part ramps back up.
-    k_warm, k_timed = max(10, K), max(40, K)
+    # GPU is first parked on a sleep kernel so that the host queues the steps
+    # before they run: the kernels then run back to back and each event pair
+    # brackets GPU time only, not host launch gaps. The first k_warm queued
+    # steps, about 25 ms of GPU work, are not timed: the kernels right after
+    # the idle sleep run slower while the part ramps back up (at 8192 x 8192
+    # LayerNorm, 2.5 ms of warm-up left its backward 25 % slower than 25 ms).
+    step_ms = st["det"]["median"]
+    k_warm = int(min(1000, max(10, K, math.ceil(25.0 / max(step_ms, 1e-3)))))
+    k_timed = max(40, K)
     rn.rmsnorm_timing_read()
     rn.rmsnorm_timing_enable(False)
     torch.cuda.synchronize()
