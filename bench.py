@@ -412,12 +412,14 @@ def dominant(wk, op, m):
 def op_summary(wk, op, m):
     st = m["stats"]["det"]
     name, nb, us = dominant(wk, op, m)
+    traffic = traffic_for(wk.name, name) if op == "fwd+bwd" else None  # counted in fwd+bwd steps
     out = {"GBps": round(m["value"], 1), "pct_of_hbm_peak": round(100 * m["value"] / HBM_PEAK_GBPS, 2),
            "ms_per_step": round(m["ms_per_step"], 5), "p10": round(st["p10"], 5),
            "p90": round(st["p90"], 5), "aa_noise": round(m["aa_noise"], 4),
            "kernel_us": {k: (round(v, 3) if v is not None else None) for k, v in m["kernel_us"].items()},
            "roofline_kernel": name,
-           "roofline_frac": round(gbps(nb, us * 1e-3) / HBM_PEAK_GBPS, 4) if us else None}
+           "roofline_frac": round(gbps(nb, us * 1e-3) / HBM_PEAK_GBPS, 4) if us else None,
+           "roofline_bytes": nb, "traffic": traffic}
     if "nondet" in m["stats"]:
         out["nondet_ms_per_step"] = round(m["stats"]["nondet"]["median"], 5)
     return out
