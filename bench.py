@@ -621,6 +621,15 @@ def main() -> int:
                 entry[o] = op_summary(w2, o, measure_op(args, torch, rn, _lib, dev, w2, o))
             if "bwd" in entry and entry["bwd"]["roofline_kernel"] == "bwd_row":
                 entry["fwd+bwd"]["roofline_frac_cold_bwd"] = entry["bwd"]["roofline_frac"]
+            wt2 = torch.bfloat16 if w2.wdtype == "bf16" else torch.float32
+            if ln:
+                entry["route"] = {"fwd": rn.rmsnorm_route_query("ln_fwd", w2.rows, w2.H, wt2),
+                                  "bwd": rn.rmsnorm_route_query("ln_bwd", w2.rows, w2.H, wt2)}
+            else:
+                entry["route"] = {"fwd": rn.rmsnorm_route_query("fwd", w2.rows, w2.H, wt2,
+                                                                residual=w2.residual),
+                                  "bwd": rn.rmsnorm_route_query("bwd", w2.rows, w2.H, wt2,
+                                                                residual=w2.residual)}
             del w2
             torch.cuda.empty_cache()
 
