@@ -98,3 +98,52 @@ def test_noalloc_refuses_more_than_its_scratch():
         assert st == -10, st
     finally:
         rn.rmsnorm_route_override("bwd")
+
+
+def test_noalloc_in_a_captured_graph():
+    """What the entry point is for: a HIP graph captures the allocation-free
+    backward (one eager call first looks the scratch address up) and every
+    replay returns the eager bits, with eager calls of another shape between
+    the replays overwriting the shared scratch."""
+    wl = synth.make(T=4096, H=4096, w_dtype="bf16", seed=43)
+    T, H = wl.T, wl.H
+    _announce(f"no-alloc graph T={T} H={H}")
+    x, dy, w = dev_bf16(wl.x).view(T, 1, H), dev_bf16(wl.dy).view(T, 1, H), dev_w(wl.w)
+    _, r32 = oracle_rstd32(wl.x, wl.w.f64, wl.eps)
+    rs = dev_f32(r32).view(T, 1)
+    dx = filled((T, 1, H))
+    dw = nan_f32(H)
+    other = synth.make(T=3000, heads=4, H=256, w_dtype="f32", seed=44)
+    ox, ody, ow = (dev_bf16(other.x).view(3000, 4, 256), dev_bf16(other.dy).view(3000, 4, 256),
+                   dev_w(other.w))
+    _, or32 = oracle_rstd32(other.x, other.w.f64, other.eps)
+    ors = dev_f32(or32).view(3000, 4)
+    odx = filled((3000, 4, 256))
+    odw = nan_f32(256)
+
+    rn.rmsnorm_bwd_strided_noalloc(dy, x, rs, w, deterministic=True, dx=dx, dw=dw)
+    torch.cuda.synchronize()
+    ref_dx, ref_dw = host_bits(dx).reshape(T, H), dw.cpu().numpy()
+    fullsize.check_dx_rows("dx (eager)", ref_dx, wl.dy, wl.x, r32.astype(np.float64), wl.w.f64)
+    _, _, dw64 = oracle.bwd(wl.dy, wl.x, r32.astype(np.float64), wl.w.f64, want_dx=False)
+    check_dw("dw (eager)", ref_dw, dw64)
+
+    g = torch.cuda.CUDAGraph()
+    cs = torch.cuda.Stream(device=DEV)
+    cs.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cs):
+        with torch.cuda.graph(g, stream=cs):
+            rn.rmsnorm_bwd_strided_noalloc(dy, x, rs, w, deterministic=True, dx=dx, dw=dw)
+    torch.cuda.synchronize()
+    for i in range(3):
+        dx.view(torch.int16).fill_(fullsize.SENTINEL)
+        dw.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(host_bits(dx).reshape(T, H), ref_dx), f"replay {i}: dx"
+        assert np.array_equal(dw.cpu().numpy().view(np.uint32), ref_dw.view(np.uint32)), f"replay {i}: dw"
+        # eager work of another shape on the same scratch between replays
+        rn.rmsnorm_bwd_strided_noalloc(ody, ox, ors, ow, deterministic=True, dx=odx, dw=odw)
+        torch.cuda.synchronize()
+        assert fullsize.unwritten(host_bits(odx)) == 0
