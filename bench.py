@@ -47,6 +47,13 @@ Timing (the pages' protocol, Cake page "Measurement", on HIP graphs):
 * per_config: fwd, bwd, fwd+bwd and 2xfwd+bwd (the pages' three timed ops
   and the metric's step) of every workload of the family, with the same
   protocol, in the same run (--no-per-config skips it);
+* flush_protocol: cross-checks of the cold-cache setting for the chosen
+  workload and op (and each workload's fwd+bwd in per_config), each a graph
+  of a single step replayed --replays times: after a 512 MiB write to a
+  separate buffer outside the timed span (the flush the pages run before
+  each timed replay), after a 512 MiB read instead, and with no flush over
+  the rotating buffer sets. Reported beside the K-step figure, never as
+  value (--no-flush-check skips them);
 * cpu_baseline: the FP64 oracle on the same work, called on row slices from
   a pool of host threads (the oracle's C code runs without the interpreter
   lock), and single-threaded beside it.
@@ -69,6 +76,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
+FLUSH_BYTES = 512 << 20
 METRIC = "RMSNorm fwd+bwd effective HBM GB/s and % of 8 TB/s peak, per (T,H)"
 DEFAULT_CONFIG = "c3_T131072_H2048_f32w_heavy"
 DEFAULT_LN_CONFIG = "ln_T8192_H4096_bf16w"
@@ -395,6 +403,68 @@ def measure_op(args, torch, rn, _lib, dev, wk, op, nondet=True):
             "K": K, "W": W, "kernel_steps": k_timed}
 
 
+def measure_flush(args, torch, dev, wk, op):
+    """Cross-checks of the cold-cache setting, each --replays replays of a
+    graph holding a single step, timed with HIP events around the replay:
+      write_flush: 512 MiB written to a separate buffer before each replay,
+        outside the span (the flush the pages run before each timed replay);
+        the step starts with the caches full of that buffer's dirty lines;
+      read_flush: the same buffer read (summed) instead, which evicts the
+        step's tensors without leaving dirty lines behind;
+      one_step_rotating: no flush; one single-step graph per buffer set,
+        replayed in rotation, so the step is as cold as in the K-step graphs
+        and only the per-replay launch cost differs from them.
+    Run after measure_op on the same workload, so every buffer set already
+    holds a forward's outputs."""
+    cur = torch.cuda.current_stream(dev)
+    step = wk.step_fn(op)
+    graphs = []
+    for s in wk.sets:
+        g = torch.cuda.CUDAGraph()
+        cs = torch.cuda.Stream(device=dev)
+        cs.wait_stream(cur)
+        with torch.cuda.stream(cs):
+            with torch.cuda.graph(g, stream=cs):
+                step(s, 1, P(torch.cuda.current_stream(dev).cuda_stream))
+        graphs.append(g)
+    torch.cuda.synchronize()
+    flush = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
+    n = max(1, args.replays)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(n)]
+    sb = wk.step_bytes(op)
+
+    def run(prep, rotate):
+        graphs[0].replay()  # untimed
+        for i in range(n):
+            g = graphs[i % len(graphs)] if rotate else graphs[0]
+            prep(i)
+            ev[i][0].record(cur)
+            g.replay()
+            ev[i][1].record(cur)
+        torch.cuda.synchronize()
+        spans = [ev[i][0].elapsed_time(ev[i][1]) for i in range(n)]
+        med = pct(spans, 0.5)
+        return {"ms_per_step": round(med, 5), "p10": round(pct(spans, 0.1), 5),
+                "p90": round(pct(spans, 0.9), 5), "value": round(gbps(sb, med), 2)}
+
+    sink = []
+
+    def read_flush(i):
+        sink.append(flush.sum())  # results kept briefly, so the reads are not elided
+        if len(sink) > 64:
+            sink.clear()
+
+    out = {"replays": n, "flush_bytes": FLUSH_BYTES, "buffer_sets": len(graphs),
+           "span": "HIP events around one replay of a one-step graph"}
+    out["write_flush"] = run(lambda i: flush.fill_(float(i & 1023)), False)
+    out["read_flush"] = run(read_flush, False)
+    out["one_step_rotating"] = run(lambda i: None, True)
+    del graphs, flush, sink
+    torch.cuda.empty_cache()
+    return out
+
+
 def dominant(wk, op, m):
     """The dominant kernel of a step: (name, algorithmic bytes, mean us)."""
     fwd_b, bwd_row_b, bwd_b = wk.bytes
@@ -516,6 +586,8 @@ def main() -> int:
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-per-config", action="store_true",
                     help="time only the chosen workload, not every workload of its family")
+    ap.add_argument("--no-flush-check", action="store_true",
+                    help="skip the flush-protocol cross-check of the chosen workload and op")
     ap.add_argument("--no-cold", action="store_true",
                     help="skip the backward-only (cold) timing of the chosen workload, so that "
                          "a kernel trace holds the in-step launches of its kernels only")
@@ -581,6 +653,10 @@ def main() -> int:
     if op != "fwd" and op != "bwd" and not args.no_cold:
         progress(f"{args.config} bwd alone: timing (cold backward)")
         cold = measure_op(args, torch, rn, _lib, dev, wk, "bwd", nondet=False)
+    flush_m = None
+    if not args.no_flush_check:
+        progress(f"{args.config} {op}: flush-protocol cross-check")
+        flush_m = measure_flush(args, torch, dev, wk, op)
     dom_name, dom_bytes, dom_us = dominant(wk, op, m)
     achieved = gbps(dom_bytes, dom_us * 1e-3)
     frac_cold = None
@@ -603,6 +679,8 @@ def main() -> int:
     per_config = {}
     if op == "fwd+bwd":
         per_config[args.config] = {"fwd+bwd": op_summary(wk, op, m)}
+        if flush_m is not None:
+            per_config[args.config]["fwd+bwd"]["flush_protocol"] = flush_m
         if cold is not None:
             per_config[args.config]["bwd"] = op_summary(wk, "bwd", cold)
     del wk
@@ -619,6 +697,9 @@ def main() -> int:
                     continue
                 progress(f"per-config {name} {o}: timing")
                 entry[o] = op_summary(w2, o, measure_op(args, torch, rn, _lib, dev, w2, o))
+            if not args.no_flush_check and "flush_protocol" not in entry["fwd+bwd"]:
+                progress(f"per-config {name} fwd+bwd: flush-protocol cross-check")
+                entry["fwd+bwd"]["flush_protocol"] = measure_flush(args, torch, dev, w2, "fwd+bwd")
             if "bwd" in entry and entry["bwd"]["roofline_kernel"] == "bwd_row":
                 entry["fwd+bwd"]["roofline_frac_cold_bwd"] = entry["bwd"]["roofline_frac"]
             wt2 = torch.bfloat16 if w2.wdtype == "bf16" else torch.float32
@@ -682,6 +763,7 @@ def main() -> int:
                      "traffic": traffic_for(args.config, dom_name) if op == "fwd+bwd" else None,
                      "algorithmic_bytes": dom_bytes,
                      "frac_cold": round(frac_cold, 4) if frac_cold is not None else None},
+        "flush_protocol": flush_m,
         "cpu_baseline": cpu,
         "route": route,
         "per_config": per_config or None,
