@@ -40,6 +40,15 @@ pytestmark = pytest.mark.gpu
 ROW_LIMIT = 2 ** 31 - 1
 
 
+@pytest.fixture(autouse=True)
+def _release_cached_memory():
+    """Each case needs up to about 150 GB of device memory: hand back what
+    earlier tests left in the caching allocator first."""
+    _free()
+    yield
+    _free()
+
+
 def _periodic(base: torch.Tensor, rows: int) -> torch.Tensor:
     """[rows, W] whose row r is base[r % p] (a fresh contiguous tensor)."""
     p = base.shape[0]
