@@ -17,13 +17,14 @@
 // operations per element and replaces the compensated FP32 sums (TwoSum
 // plus periodic FP64 fold) that the pages use on hardware with slow FP64.
 //
-// How the per-block sums meet (the only difference between the modes):
-// * deterministic: block b takes the row tiles b, b + P, b + 2P, ..., where
-//   P (the grid) is a function of the shape only; it adds them in that order,
-//   combines its row slots in slot order and writes its partial row;
-//   k_dw_reduce then sums the P partials in a fixed order. No step depends
-//   on scheduling or on the CU count.
-// * atomic (non-deterministic): the same blocks add their sums into an FP64
+// How the per-block sums meet:
+// * fixed order (both modes, as the route table has them): block b takes the
+//   row tiles b, b + P, b + 2P, ..., where P (the grid) is a function of the
+//   shape only; it adds them in that order, combines its row slots in slot
+//   order and writes its partial row; k_dw_reduce then sums the P partials
+//   in a fixed order. No step depends on scheduling or on the CU count.
+// * atomic (the non-deterministic mode, only through a route override, as
+//   it measured slower): the same blocks add their sums into an FP64
 //   accumulator with hardware atomics; the last block to finish (a ticket
 //   counter) converts it to FP32 dw.
 // * small T: one launch of k_bwd_small — column tasks sum whole columns over

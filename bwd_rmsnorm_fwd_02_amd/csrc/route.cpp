@@ -9,9 +9,10 @@
 // backward routes", "Changed windows by reason"). The kinds kept here are
 // the ones that still hold on gfx950: a column-task kernel for small T (the
 // page serves T from 1 to 64 with its column-task kernel), and a row kernel
-// with per-block dw partials plus a reduce (the "chunk-partials pair"), or
-// with atomics. No dw-accuracy cut is needed above that: FP64 dw
-// accumulation keeps every shape inside the budget.
+// with per-block dw partials plus a reduce (the "chunk-partials pair") for
+// both modes, or with atomics when an override asks for them. No
+// dw-accuracy cut is needed above that: FP64 dw accumulation keeps every
+// shape inside the budget.
 #include <string.h>
 
 #include "rmsn_internal.h"
