@@ -5,8 +5,8 @@ The hand-picked shapes elsewhere pin each route edge one by one; these cases
 sample the whole shape space the route table covers instead: token counts
 from 1 to 40000 (log-uniform, so the small-T column-task route and the row
 route both come up), every multiple of 8 from 8 to 16384 as the width, both
-weight dtypes, and the plain, residual, per-head, strided and LayerNorm
-forms. Every output buffer is filled with NaN first, so an element the
+weight dtypes, and the plain, residual (contiguous and over views),
+per-head, strided, recompute-backward, allocation-free and LayerNorm forms. Every output buffer is filled with NaN first, so an element the
 kernels never write fails; every element of y, dx (dh), h and every row's
 statistics are compared, and dw (dgamma, dbeta) is checked at the forward's
 FP32 statistics and at the FP64 ones, in both modes. The case list comes
@@ -23,27 +23,30 @@ import torch
 import bwd_rmsnorm_fwd_02_amd as rn
 import oracle
 from tests import fullsize, synth
-from tests.parity import check_dw, check_ln_stats, check_rstd, oracle_rstd32
+from tests.parity import (check_dw, check_dx, check_ln_stats, check_rstd, dx_bound,
+                          oracle_rstd32, to_f64)
 from tests.test_parity_gpu import (DEV, _announce, dev_bf16, dev_f32, dev_w, filled, host_bits,
                                    nan_f32)
 
 MAX_ELEMS = 1 << 21   # rows x H per case, so the oracle takes well under a second
 
 
-def _draw_cases(seed: int = 20261203, n: int = 48):
+def _draw_cases(seed: int = 20261203, n: int = 72):
     rng = np.random.default_rng(seed)
-    forms = ["plain", "plain", "residual", "heads", "strided", "layernorm"]
+    forms = ["plain", "plain", "residual", "residual_views", "heads", "strided", "recompute",
+             "noalloc", "layernorm"]
     cases = []
     for i in range(n):
         form = forms[int(rng.integers(len(forms)))]
         H = 8 * int(round(math.exp(rng.uniform(0.0, math.log(2048.0)))))
-        heads = int(rng.integers(2, 9)) if form in ("heads", "strided") else 1
+        viewed = form in ("heads", "strided", "residual_views", "recompute", "noalloc")
+        heads = int(rng.integers(1 if form != "heads" else 2, 9)) if viewed else 1
         t_max = max(1, min(40000, MAX_ELEMS // (H * heads)))
         T = int(round(math.exp(rng.uniform(0.0, math.log(t_max)))))
         T = max(1, min(T, t_max))
         wdt = "bf16" if rng.integers(2) else "f32"
-        extra = int(rng.integers(0, 9)) * 8 if form == "strided" else 0
-        with_dres = bool(rng.integers(2)) if form == "residual" else False
+        extra = int(rng.integers(0, 9)) * 8 if viewed and form != "heads" else 0
+        with_dres = bool(rng.integers(2)) if form in ("residual", "residual_views") else False
         cases.append((i, form, T, heads, H, wdt, extra, with_dres))
     return cases
 
@@ -59,8 +62,9 @@ def _ids(c):
 
 def _rms_case(form, T, heads, H, wdt, extra, with_dres, seed):
     residual = form == "residual"
+    strided = form in ("strided", "noalloc")
     wl = synth.make(T=T, H=H, w_dtype=wdt, seed=seed, heads=heads, residual=residual,
-                    with_dres=with_dres, strided_row=(heads * H + extra) if form == "strided" else 0)
+                    with_dres=with_dres, strided_row=(heads * H + extra) if strided else 0)
     rows = wl.rows
     w = dev_w(wl.w)
     # ---- forward
@@ -80,7 +84,7 @@ def _rms_case(form, T, heads, H, wdt, extra, with_dres, seed):
             assert np.array_equal(host_bits(h), src), "h = BF16(x + r) not bit-exact"
         rs_got = rstd.cpu().numpy()
     else:
-        if form == "strided":
+        if strided:
             xbuf = dev_bf16(wl.xbuf)
             xv = xbuf[:, : heads * H].unflatten(1, (heads, H))
         else:
@@ -114,11 +118,11 @@ def _rms_case(form, T, heads, H, wdt, extra, with_dres, seed):
         else:
             dxbuf = filled((T, heads * H + extra))
             dxv = dxbuf[:, : heads * H].unflatten(1, (heads, H))
-            rn.rmsnorm_bwd_strided(dev_bf16(wl.dy).view(T, heads, H), xv,
-                                   dev_f32(r32).view(T, heads), w, deterministic=det,
-                                   dx=dxv, dw=dw)
+            call = rn.rmsnorm_bwd_strided_noalloc if form == "noalloc" else rn.rmsnorm_bwd_strided
+            call(dev_bf16(wl.dy).view(T, heads, H), xv, dev_f32(r32).view(T, heads), w,
+                 deterministic=det, dx=dxv, dw=dw)
         torch.cuda.synchronize()
-        if form in ("heads", "strided"):
+        if form in ("heads", "strided", "noalloc"):
             full = host_bits(dxbuf)
             if extra:
                 assert np.all(full[:, heads * H:] == fullsize.SENTINEL), "gap columns written"
@@ -132,6 +136,89 @@ def _rms_case(form, T, heads, H, wdt, extra, with_dres, seed):
         check_dw(f"dw det={det} (FP64 rstd)", dwh, dw64_i)
         outs[det] = (dxbits, dwh)
     assert np.array_equal(outs[True][0], outs[False][0]), "dx differs between modes"
+
+
+def _wide(bits, T, heads, H, gap):
+    """A [T, heads*H + gap] buffer: NaN fill, with `bits` (rows of H) in the
+    first heads*H columns if given; returns (buffer, [T, heads, H] view)."""
+    buf = filled((T, heads * H + gap))
+    view = buf[:, : heads * H].unflatten(1, (heads, H))
+    if bits is not None:
+        view.copy_(dev_bf16(bits).view(T, heads, H))
+    return buf, view
+
+
+def _rows_of(buf, T, heads, H, gap):
+    full = host_bits(buf)
+    if gap:
+        assert np.all(full[:, heads * H:] == fullsize.SENTINEL), "gap columns written"
+    return np.ascontiguousarray(full[:, : heads * H]).reshape(T * heads, H)
+
+
+def _residual_views_case(T, heads, H, wdt, gap, with_dres, seed):
+    wl = synth.make(T=T, H=H, w_dtype=wdt, seed=seed, heads=heads, residual=True,
+                    with_dres=with_dres)
+    w = dev_w(wl.w)
+    _, xv = _wide(wl.x, T, heads, H, gap)
+    _, rv = _wide(wl.r, T, heads, H, gap)
+    hb, hv = _wide(None, T, heads, H, gap)
+    yb, yv = _wide(None, T, heads, H, gap)
+    rstd = nan_f32(T * heads).view(T, heads)
+    rn.rmsnorm_residual_fwd_strided(xv, rv, w, wl.eps, h=hv, y=yv, rstd=rstd)
+    torch.cuda.synchronize()
+    h_ref = oracle.residual_add(wl.x, wl.r)
+    assert np.array_equal(_rows_of(hb, T, heads, H, gap), h_ref), "h = BF16(x + r) not bit-exact"
+    r64, r32 = oracle_rstd32(h_ref, wl.w.f64, wl.eps)
+    check_rstd("rstd", rstd.cpu().numpy().reshape(-1), r64)
+    fullsize.check_y_rows("y", _rows_of(yb, T, heads, H, gap), h_ref, wl.w.f64, wl.eps)
+    r32_64 = r32.astype(np.float64)
+    _, _, dw64 = oracle.bwd(wl.dy, h_ref, r32_64, wl.w.f64, want_dx=False)
+    _, _, dw64_i = oracle.bwd(wl.dy, h_ref, r64, wl.w.f64, want_dx=False)
+    _, dyv = _wide(wl.dy, T, heads, H, gap)
+    _, hin = _wide(h_ref, T, heads, H, gap)
+    drv = _wide(wl.dres, T, heads, H, gap)[1] if with_dres else None
+    outs = []
+    for det in (True, False):
+        dhb, dhv = _wide(None, T, heads, H, gap)
+        dw = nan_f32(H)
+        rn.rmsnorm_residual_bwd_strided(dyv, hin, dev_f32(r32).view(T, heads), w, dres=drv,
+                                        deterministic=det, dh=dhv, dw=dw)
+        torch.cuda.synchronize()
+        outs.append(_rows_of(dhb, T, heads, H, gap))
+        fullsize.check_dx_rows(f"dh det={det}", outs[-1], wl.dy, h_ref, r32_64, wl.w.f64,
+                               wl.dres if with_dres else None)
+        check_dw(f"dw det={det} (forward's rstd)", dw.cpu().numpy(), dw64)
+        check_dw(f"dw det={det} (FP64 rstd)", dw.cpu().numpy(), dw64_i)
+    assert np.array_equal(outs[0], outs[1]), "dh differs between modes"
+
+
+def _recompute_case(T, heads, H, wdt, gap, seed):
+    """The backward that recomputes rstd from x: dx within one ulp, or ulp
+    plus the plain bound widened by the effect of a one-ulp FP32 difference
+    in rstd (d(dx)/d(rstd) = g - 3 xhat c)."""
+    wl = synth.make(T=T, H=H, w_dtype=wdt, seed=seed, heads=heads)
+    w = dev_w(wl.w)
+    _, xv = _wide(wl.x, T, heads, H, gap)
+    _, dyv = _wide(wl.dy, T, heads, H, gap)
+    r64, r32 = oracle_rstd32(wl.x, wl.w.f64, wl.eps)
+    r32_64 = r32.astype(np.float64)
+    dx64, c64, dw64 = oracle.bwd(wl.dy, wl.x, r32_64, wl.w.f64)
+    _, _, dw64_i = oracle.bwd(wl.dy, wl.x, r64, wl.w.f64, want_dx=False)
+    x64, dy64 = to_f64(wl.x), to_f64(wl.dy)
+    E = dx_bound(x64, dy64, wl.w.f64, r32_64, c64, H)
+    g = dy64 * wl.w.f64[None, :]
+    E = E + 2.0 ** -23 * r32_64[:, None] * (np.abs(g) + 3.0 * np.abs(x64 * r32_64[:, None] * c64[:, None]))
+    outs = []
+    for det in (True, False):
+        dxb, dxv = _wide(None, T, heads, H, gap)
+        dw = nan_f32(H)
+        rn.rmsnorm_bwd_recompute(dyv, xv, w, wl.eps, deterministic=det, dx=dxv, dw=dw)
+        torch.cuda.synchronize()
+        outs.append(_rows_of(dxb, T, heads, H, gap))
+        check_dx(f"dx det={det}", outs[-1], dx64, E)
+        check_dw(f"dw det={det} (forward's rstd)", dw.cpu().numpy(), dw64)
+        check_dw(f"dw det={det} (FP64 rstd)", dw.cpu().numpy(), dw64_i)
+    assert np.array_equal(outs[0], outs[1]), "dx differs between modes"
 
 
 def _ln_case(T, H, wdt, seed):
@@ -170,6 +257,10 @@ def test_random_shape(case):
     seed = 1000 + i
     if form == "layernorm":
         _ln_case(T, H, wdt, seed)
+    elif form == "residual_views":
+        _residual_views_case(T, heads, H, wdt, extra, with_dres, seed)
+    elif form == "recompute":
+        _recompute_case(T, heads, H, wdt, extra, seed)
     else:
         _rms_case(form, T, heads, H, wdt, extra, with_dres, seed)
 
@@ -179,7 +270,8 @@ def test_case_list_spans_the_routes():
     form, widths on both sides of 2048 and partial rows on both sides of the
     8192-row precision switch."""
     forms = {c[1] for c in CASES}
-    assert forms == {"plain", "residual", "heads", "strided", "layernorm"}
+    assert forms == {"plain", "residual", "residual_views", "heads", "strided", "recompute",
+                     "noalloc", "layernorm"}
     assert {c[5] for c in CASES} == {"bf16", "f32"}
     rows = [c[2] * c[3] for c in CASES if c[1] != "layernorm"]
     assert min(rows) <= 64 < max(rows)
