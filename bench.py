@@ -308,7 +308,7 @@ def measure_op(args, torch, rn, _lib, dev, wk, op, nondet=True):
     # has its inputs; then the eager warm-up and a reference result for set 0
     for s in sets:
         wk.fwd(s, sp)
-    for i in range(W):
+    for i in range(max(1, W)):  # at least one step: set 0's outputs are the reference
         step(sets[i % n_sets], 1, sp)
     torch.cuda.synchronize()
     ref = {k: sets[0][k].clone() for k in out_keys}
@@ -600,6 +600,9 @@ def main() -> int:
                     help="only run a plain device copy of BYTES bytes 10 times (the reference "
                          "kernel for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE) and exit")
     args = ap.parse_args()
+    if args.steps < 1 or args.warmup < 0 or args.replays < 1 or args.rounds < 1:
+        print("--steps, --replays and --rounds take 1 or more, --warmup 0 or more", file=sys.stderr)
+        return 2
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this RMSNorm path has no multi-GPU step "
