@@ -435,6 +435,95 @@ def rmsnorm_residual_bwd_strided(dy: torch.Tensor, h: torch.Tensor, rstd: torch.
     return dh, dw
 
 
+# ------------------------------------------------------- deferred dw reduce
+
+def rmsnorm_bwd_partials_bytes(rows: int, H: int, w_dtype: torch.dtype) -> int:
+    wd = _lib.RMSN_BF16 if w_dtype == torch.bfloat16 else _lib.RMSN_F32
+    return int(_lib.load().rmsnorm_bwd_partials_bytes(rows, H, wd))
+
+
+def _partials(dev, rows, H, w, partials):
+    need = rmsnorm_bwd_partials_bytes(rows, H, w.dtype)
+    if partials is None:
+        raw = torch.empty(need + 256, dtype=torch.uint8, device=dev)
+        partials = raw[(-raw.data_ptr()) % 256:]
+    nbytes = _ws_bytes("partials", partials, dev)
+    return partials, nbytes
+
+
+def rmsnorm_bwd_strided_partials(dy: torch.Tensor, x: torch.Tensor, rstd: torch.Tensor,
+                                 w: torch.Tensor, dx: Optional[torch.Tensor] = None,
+                                 partials: Optional[torch.Tensor] = None):
+    """The deterministic backward over views without its dw reduction: dx,
+    and a uint8 buffer of dw partial rows for rmsnorm_dw_reduce_batch.
+    Returns (dx, partials)."""
+    _need_bf16("x", x)
+    dev = x.device
+    xv = _view(x)
+    rows = xv.T * xv.heads
+    dyv = _need_view("dy", dy, dev, x.shape)
+    _need_f32("rstd", rstd, dev, rows)
+    wd = _need_weight("w", w, dev, xv.H)
+    if dx is None:
+        dx = torch.empty(x.shape, dtype=torch.bfloat16, device=dev)
+    dxv = _need_view("dx", dx, dev, x.shape)
+    if partials is not None:
+        _ws_bytes("partials", partials, dev)
+    _need_gpu(dev)
+    partials, nbytes = _partials(dev, rows, xv.H, w, partials)
+    _lib.check(_lib.load().rmsnorm_bwd_strided_partials(_ptr(dy), dyv, _ptr(x), xv, _ptr(rstd),
+                                                        _ptr(w), wd, _ptr(dx), dxv, _ptr(partials),
+                                                        nbytes, _stream(dev)))
+    return dx, partials
+
+
+def rmsnorm_residual_bwd_strided_partials(dy: torch.Tensor, h: torch.Tensor, rstd: torch.Tensor,
+                                          w: torch.Tensor, dres: Optional[torch.Tensor] = None,
+                                          dh: Optional[torch.Tensor] = None,
+                                          partials: Optional[torch.Tensor] = None):
+    """The residual form of rmsnorm_bwd_strided_partials. Returns (dh, partials)."""
+    _need_bf16("h", h)
+    dev = h.device
+    hv = _view(h)
+    rows = hv.T * hv.heads
+    dyv = _need_view("dy", dy, dev, h.shape)
+    dresv = _need_view("dres", dres, dev, h.shape) if dres is not None else View(0, 1, hv.H, 0, 0)
+    _need_f32("rstd", rstd, dev, rows)
+    wd = _need_weight("w", w, dev, hv.H)
+    if dh is None:
+        dh = torch.empty(h.shape, dtype=torch.bfloat16, device=dev)
+    dhv = _need_view("dh", dh, dev, h.shape)
+    if partials is not None:
+        _ws_bytes("partials", partials, dev)
+    _need_gpu(dev)
+    partials, nbytes = _partials(dev, rows, hv.H, w, partials)
+    _lib.check(_lib.load().rmsnorm_residual_bwd_strided_partials(
+        _ptr(dy), dyv, _ptr(h), hv, _ptr(dres), dresv, _ptr(rstd), _ptr(w), wd, _ptr(dh), dhv,
+        _ptr(partials), nbytes, _stream(dev)))
+    return dh, partials
+
+
+def rmsnorm_dw_reduce_batch(jobs) -> None:
+    """Reduce the partial rows of earlier deferred backward calls into their
+    dw, in one launch per 32 jobs of each partial precision. jobs: a list of
+    (partials, rows, H, w_dtype, dw) with rows = T * heads of that call and
+    dw an [H] FP32 tensor written in full."""
+    n = len(jobs)
+    arr = (_lib.DwJob * max(n, 1))()
+    dev = None
+    for i, (partials, rows, H, w_dtype, dw) in enumerate(jobs):
+        _need_tensor("partials", partials)
+        dev = partials.device if dev is None else dev
+        nbytes = _ws_bytes("partials", partials, dev)
+        _need_f32("dw", dw, dev, int(H))
+        wd = _lib.RMSN_BF16 if w_dtype == torch.bfloat16 else _lib.RMSN_F32
+        arr[i] = _lib.DwJob(partials.data_ptr(), nbytes, int(rows), int(H), wd, dw.data_ptr())
+    if n == 0:
+        return
+    _need_gpu(dev)
+    _lib.check(_lib.load().rmsnorm_dw_reduce_batch(arr, n, _stream(dev)))
+
+
 # ---------------------------------------------------------------- LayerNorm
 
 def layernorm_fwd(x: torch.Tensor, gamma: torch.Tensor, beta: Optional[torch.Tensor] = None,

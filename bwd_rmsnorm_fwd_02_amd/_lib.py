@@ -44,12 +44,20 @@ EXPORTS = [
     "rmsnorm_status_string",
     "rmsnorm_route_query", "rmsnorm_route_override", "rmsnorm_timing_enable",
     "rmsnorm_timing_read", "layernorm_fwd", "layernorm_bwd_workspace_bytes", "layernorm_bwd",
+    "rmsnorm_bwd_partials_bytes", "rmsnorm_bwd_strided_partials",
+    "rmsnorm_residual_bwd_strided_partials", "rmsnorm_dw_reduce_batch",
 ]
 
 
 class View(ctypes.Structure):
     _fields_ = [("T", ctypes.c_int64), ("heads", ctypes.c_int64), ("H", ctypes.c_int64),
                 ("stride_t", ctypes.c_int64), ("stride_h", ctypes.c_int64)]
+
+
+class DwJob(ctypes.Structure):
+    _fields_ = [("partials", ctypes.c_void_p), ("partials_bytes", ctypes.c_size_t),
+                ("rows", ctypes.c_int64), ("H", ctypes.c_int64), ("w_dtype", ctypes.c_int),
+                ("dw", ctypes.c_void_p)]
 
 
 class RouteInfo(ctypes.Structure):
@@ -125,6 +133,11 @@ def load() -> ctypes.CDLL:
         "layernorm_fwd": [p, p, p, i32, f32, p, p, p, i64, i64, p],
         "layernorm_bwd_workspace_bytes": [i64, i64, i32, i32],
         "layernorm_bwd": [p, p, p, p, p, i32, i32, p, p, p, i64, i64, p, sz, p],
+        "rmsnorm_bwd_partials_bytes": [i64, i64, i32],
+        "rmsnorm_bwd_strided_partials": [p, View, p, View, p, p, i32, p, View, p, sz, p],
+        "rmsnorm_residual_bwd_strided_partials": [p, View, p, View, p, View, p, p, i32, p, View,
+                                                  p, sz, p],
+        "rmsnorm_dw_reduce_batch": [ctypes.POINTER(DwJob), i32, p],
     }
     for name, args in sig.items():
         f = getattr(lib, name)
@@ -132,6 +145,7 @@ def load() -> ctypes.CDLL:
         f.restype = ctypes.c_int
     lib.rmsnorm_bwd_workspace_bytes.restype = ctypes.c_size_t
     lib.layernorm_bwd_workspace_bytes.restype = ctypes.c_size_t
+    lib.rmsnorm_bwd_partials_bytes.restype = ctypes.c_size_t
     lib.rmsnorm_status_string.restype = ctypes.c_char_p
     _lib = lib
     return lib

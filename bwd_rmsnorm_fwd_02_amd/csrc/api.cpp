@@ -6,6 +6,7 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <algorithm>
 #include <vector>
 
 #include "rmsn_internal.h"
@@ -215,11 +216,34 @@ int fwd_impl(const void* x, const rmsn_view_t& xv, const void* r, const rmsn_vie
 
 // --------------------------------------------------------------- backward
 
+// Layout of the partial rows a deferred backward leaves for (rows, H): P
+// rows of H FP64 or FP32 values in `bytes` bytes. Token counts up to the
+// column-task limit leave one FP32 row holding the final dw.
+int deferred_layout(int64_t rows, int64_t H, rmsn_dtype_t wdt, int64_t* P, int* f64,
+                    size_t* bytes) {
+    Route rt;
+    const int st = route(1, rows, H, wdt, 1, kFormPlain, &rt);
+    if (st != RMSN_OK) return st;
+    if (rt.r.kind != RMSN_KIND_BWD_ROW_DET) {
+        *P = 1;
+        *f64 = 0;
+        *bytes = ((size_t)H * 4 + 255) & ~(size_t)255;
+        return RMSN_OK;
+    }
+    *P = rt.r.partials;
+    *f64 = rt.r.partial_f64;
+    *bytes = rt.workspace;
+    return RMSN_OK;
+}
+
+// defer: leave the dw partial rows in `ws` (the caller's, laid out as
+// deferred_layout says) instead of reducing them into dw, which is unused.
 int bwd_impl(const void* dy, const rmsn_view_t& dyv, const void* x, const rmsn_view_t& xv,
              const void* dres, const rmsn_view_t* resv, const float* rstd, const void* w,
              rmsn_dtype_t wdt, int det, void* dx, const rmsn_view_t& dxv, float* dw,
-             void* ws, size_t ws_bytes, int form, float eps, hipStream_t s) {
+             void* ws, size_t ws_bytes, int form, float eps, hipStream_t s, bool defer = false) {
     const bool residual = form == kFormResidual;
+    if (defer) det = 1;
     const bool rc = form == kFormRecompute;  // rstd recomputed from x, none passed
     int st;
     if ((st = check_dtype(wdt)) != RMSN_OK) return st;
@@ -234,8 +258,23 @@ int bwd_impl(const void* dy, const rmsn_view_t& dyv, const void* x, const rmsn_v
     }
     const int64_t rows = xv.T * xv.heads;
     const int64_t H = xv.H;
-    if (!dw) return RMSN_ERR_NULL;
-    if (!aligned(dw, 4)) return RMSN_ERR_ALIGN;
+    if (defer) {
+        int64_t P;
+        int f64;
+        size_t need;
+        if ((st = deferred_layout(rows, H, wdt, &P, &f64, &need)) != RMSN_OK) return st;
+        if (!ws || !aligned(ws, 256) || ws_bytes < need) return RMSN_ERR_WORKSPACE;
+        if (rows == 0) {
+            // one FP32 partial row of zeros: the column sum over no rows
+            timer_begin(RMSN_TIMER_INIT, s);
+            st = launch_fill_zero(ws, (size_t)H * 4, s);
+            timer_end(RMSN_TIMER_INIT, s);
+            return st;
+        }
+    } else {
+        if (!dw) return RMSN_ERR_NULL;
+        if (!aligned(dw, 4)) return RMSN_ERR_ALIGN;
+    }
     if (rows == 0) {
         // the column sum over zero rows is zero
         timer_begin(RMSN_TIMER_INIT, s);
@@ -256,7 +295,7 @@ int bwd_impl(const void* dy, const rmsn_view_t& dyv, const void* x, const rmsn_v
     const Span sx = span_of(x, ex, 2), sdy = span_of(dy, edy, 2), sdx = span_of(dx, edx, 2);
     const Span sw = span_of(w, H, wsize(wdt));
     const Span srs = rc ? Span{0, 0} : span_of(rstd, rows, 4);
-    const Span sdw = span_of(dw, H, 4);
+    const Span sdw = defer ? Span{0, 0} : span_of(dw, H, 4);
     const Span sres = dres ? span_of(dres, eres, 2) : Span{0, 0};
     if (overlap(sdx, sx) || overlap(sdx, sdy) || overlap(sdx, sw) || overlap(sdx, srs) ||
         overlap(sdx, sdw) || overlap(sdx, sres))
@@ -266,9 +305,13 @@ int bwd_impl(const void* dy, const rmsn_view_t& dyv, const void* x, const rmsn_v
 
     Route rt;
     if ((st = route(1, rows, H, wdt, det, form, &rt)) != RMSN_OK) return st;
-    if (rt.workspace > 0) {
-        if (!ws || !aligned(ws, 256) || ws_bytes < rt.workspace) return RMSN_ERR_WORKSPACE;
-        const Span sws = span_of(ws, (int64_t)rt.workspace, 1);
+    // a deferred call's partial rows need room even where the route itself
+    // needs no workspace (the column-task kernel's one dw row)
+    const size_t ws_need = defer ? (rt.workspace > (size_t)H * 4 ? rt.workspace : (size_t)H * 4)
+                                 : rt.workspace;
+    if (ws_need > 0) {
+        if (!ws || !aligned(ws, 256) || ws_bytes < ws_need) return RMSN_ERR_WORKSPACE;
+        const Span sws = span_of(ws, (int64_t)ws_need, 1);
         if (overlap(sws, sx) || overlap(sws, sdy) || overlap(sws, sdx) || overlap(sws, sw) ||
             overlap(sws, srs) || overlap(sws, sdw) || overlap(sws, sres))
             return RMSN_ERR_ALIAS;
@@ -296,6 +339,7 @@ int bwd_impl(const void* dy, const rmsn_view_t& dyv, const void* x, const rmsn_v
     p.eps = eps;
 
     if (rt.r.kind == RMSN_KIND_BWD_COLTASK) {
+        if (defer) p.dw = static_cast<float*>(ws);  // the one partial row
         p.ncol_blocks = (int32_t)rt.r.reduce_grid;
         p.col_splits = 8;
         timer_begin(RMSN_TIMER_BWD_SMALL, s);
@@ -308,7 +352,7 @@ int bwd_impl(const void* dy, const rmsn_view_t& dyv, const void* x, const rmsn_v
         timer_begin(RMSN_TIMER_BWD_ROW, s);
         st = launch_bwd_row(p, rt, wdt, form, s);
         timer_end(RMSN_TIMER_BWD_ROW, s);
-        if (st != RMSN_OK) return st;
+        if (st != RMSN_OK || defer) return st;
         timer_begin(RMSN_TIMER_DW_REDUCE, s);
         st = launch_dw_reduce(p, rt, s);
         timer_end(RMSN_TIMER_DW_REDUCE, s);
@@ -535,6 +579,95 @@ int rmsnorm_residual_bwd_strided(const void* dy, rmsn_view_t dyv, const void* h,
                                  size_t workspace_bytes, hipStream_t stream) {
     return bwd_impl(dy, dyv, h, hv, dres, dres ? &dresv : nullptr, rstd, w, w_dtype, deterministic,
                     dh, dhv, dw, workspace, workspace_bytes, kFormResidual, 0.f, stream);
+}
+
+size_t rmsnorm_bwd_partials_bytes(int64_t rows, int64_t H, rmsn_dtype_t w_dtype) {
+    int64_t P;
+    int f64;
+    size_t bytes;
+    if (deferred_layout(rows, H, w_dtype, &P, &f64, &bytes) != RMSN_OK) return 0;
+    return bytes;
+}
+
+int rmsnorm_bwd_strided_partials(const void* dy, rmsn_view_t dyv, const void* x, rmsn_view_t xv,
+                                 const float* rstd, const void* w, rmsn_dtype_t w_dtype, void* dx,
+                                 rmsn_view_t dxv, void* partials, size_t partials_bytes,
+                                 hipStream_t stream) {
+    return bwd_impl(dy, dyv, x, xv, nullptr, nullptr, rstd, w, w_dtype, 1, dx, dxv, nullptr,
+                    partials, partials_bytes, kFormPlain, 0.f, stream, true);
+}
+
+int rmsnorm_residual_bwd_strided_partials(const void* dy, rmsn_view_t dyv, const void* h,
+                                          rmsn_view_t hv, const void* dres, rmsn_view_t dresv,
+                                          const float* rstd, const void* w, rmsn_dtype_t w_dtype,
+                                          void* dh, rmsn_view_t dhv, void* partials,
+                                          size_t partials_bytes, hipStream_t stream) {
+    return bwd_impl(dy, dyv, h, hv, dres, dres ? &dresv : nullptr, rstd, w, w_dtype, 1, dh, dhv,
+                    nullptr, partials, partials_bytes, kFormResidual, 0.f, stream, true);
+}
+
+int rmsnorm_dw_reduce_batch(const rmsn_dw_job_t* jobs, int n, hipStream_t stream) {
+    if (n < 0) return RMSN_ERR_SHAPE;
+    if (n == 0) return RMSN_OK;
+    if (!jobs) return RMSN_ERR_NULL;
+    // validate every job, and that no dw overlaps any job's partials or
+    // another dw, before anything is enqueued
+    std::vector<DwJob> f32, f64;
+    std::vector<Span> parts, dws;
+    for (int i = 0; i < n; ++i) {
+        const rmsn_dw_job_t& jb = jobs[i];
+        int st;
+        if ((st = check_dtype(jb.w_dtype)) != RMSN_OK) return st;
+        if (jb.H < kVec || jb.H > kMaxH || jb.H % kVec != 0 || jb.rows < 0 || jb.rows > INT32_MAX)
+            return RMSN_ERR_SHAPE;
+        if (!jb.partials || !jb.dw) return RMSN_ERR_NULL;
+        if (!aligned(jb.partials, 16) || !aligned(jb.dw, 4)) return RMSN_ERR_ALIGN;
+        int64_t P;
+        int pf64;
+        size_t bytes;
+        if ((st = deferred_layout(jb.rows, jb.H, jb.w_dtype, &P, &pf64, &bytes)) != RMSN_OK) return st;
+        const size_t used = (size_t)P * (size_t)jb.H * (pf64 ? 8 : 4);
+        if (jb.partials_bytes < used) return RMSN_ERR_WORKSPACE;
+        parts.push_back(span_of(jb.partials, (int64_t)used, 1));
+        dws.push_back(span_of(jb.dw, jb.H, 4));
+        DwJob d;
+        d.part = jb.partials;
+        d.P = P;
+        d.H = (int32_t)jb.H;
+        d.f64 = pf64;
+        d.dw = jb.dw;
+        d.block0 = 0;
+        (pf64 ? f64 : f32).push_back(d);
+    }
+    for (int i = 0; i < n; ++i) {
+        for (int k = 0; k < n; ++k) {
+            if (overlap(dws[i], parts[k])) return RMSN_ERR_ALIAS;
+            if (k != i && overlap(dws[i], dws[k])) return RMSN_ERR_ALIAS;
+        }
+    }
+    // one launch per precision and per kMaxBatchJobs jobs; job blocks as in
+    // the single reduce (16-byte chunks of kReduceChunks per block)
+    for (std::vector<DwJob>* group : {&f32, &f64}) {
+        for (size_t at = 0; at < group->size(); at += kMaxBatchJobs) {
+            DwJobs t;
+            memset(&t, 0, sizeof t);
+            int64_t blocks = 0;
+            const size_t m = std::min(group->size() - at, (size_t)kMaxBatchJobs);
+            for (size_t q = 0; q < m; ++q) {
+                DwJob d = (*group)[at + q];
+                d.block0 = blocks;
+                const int64_t psize = d.f64 ? 8 : 4;
+                blocks += (d.H * psize + 16 * kReduceChunks - 1) / (16 * kReduceChunks);
+                t.j[q] = d;
+            }
+            t.n = (int32_t)m;
+            timer_begin(RMSN_TIMER_DW_REDUCE, stream);
+            const int st = launch_dw_reduce_batch(t, blocks, stream);
+            timer_end(RMSN_TIMER_DW_REDUCE, stream);
+            if (st != RMSN_OK) return st;
+        }
+    }
+    return RMSN_OK;
 }
 
 int layernorm_fwd(const void* x, const void* gamma, const void* beta, rmsn_dtype_t w_dtype,

@@ -13,17 +13,16 @@ namespace rmsn {
 // (LayerNorm's dgamma and dbeta share one partial row); split is a multiple
 // of the chunk width.
 template <typename PT, int CC>
-__global__ void __launch_bounds__(kReduceThreads) k_dw_reduce(const PT* __restrict__ part, int64_t P,
-                                                              int32_t H, float* __restrict__ dw,
-                                                              float* __restrict__ out1, int32_t split) {
+__device__ __forceinline__ void dw_reduce_block(const PT* __restrict__ part, int64_t P, int32_t H,
+                                                float* __restrict__ dw, float* __restrict__ out1,
+                                                int32_t split, int64_t blk, double* sm_red) {
     constexpr int CPC = 16 / sizeof(PT);  // columns per 16-byte chunk
     constexpr int NCOL = CC * CPC;        // columns per block
     constexpr int NW = kReduceThreads / 64;
     constexpr int S = kReduceThreads / CC;
-    __shared__ double sm_red[NW][NCOL];
     const int cc = threadIdx.x % CC;
     const int s = threadIdx.x / CC;
-    const int64_t col0 = ((int64_t)blockIdx.x * CC + cc) * CPC;
+    const int64_t col0 = (blk * CC + cc) * CPC;
     const bool col_ok = col0 < H;
     double a[CPC];
 #pragma unroll
@@ -68,22 +67,65 @@ __global__ void __launch_bounds__(kReduceThreads) k_dw_reduce(const PT* __restri
     const int wave = threadIdx.x >> 6;
     if ((threadIdx.x & 63) < CC) {
 #pragma unroll
-        for (int e = 0; e < CPC; ++e) sm_red[wave][cc * CPC + e] = a[e];
+        for (int e = 0; e < CPC; ++e) sm_red[wave * NCOL + cc * CPC + e] = a[e];
     }
     __syncthreads();
     // chunks are whole columns of one side of split (H and split are
     // multiples of 8 columns), so the per-column tests match the chunk's
     if (threadIdx.x < NCOL) {
         const int c = threadIdx.x;
-        const int64_t col = (int64_t)blockIdx.x * NCOL + c;
+        const int64_t col = blk * NCOL + c;
         if (col < H) {
             double t = 0.0;
 #pragma unroll
-            for (int w = 0; w < NW; ++w) t += sm_red[w][c];
+            for (int w = 0; w < NW; ++w) t += sm_red[w * NCOL + c];
             float* dst = col < split ? dw + col : out1 + (col - split);
             *dst = (float)t;
         }
     }
+}
+
+template <typename PT, int CC>
+__global__ void __launch_bounds__(kReduceThreads) k_dw_reduce(const PT* __restrict__ part, int64_t P,
+                                                              int32_t H, float* __restrict__ dw,
+                                                              float* __restrict__ out1, int32_t split) {
+    __shared__ double sm_red[(kReduceThreads / 64) * CC * (16 / sizeof(PT))];
+    dw_reduce_block<PT, CC>(part, P, H, dw, out1, split, (int64_t)blockIdx.x, sm_red);
+}
+
+// The same block body behind a call (the batched kernel calls it: inlining
+// it there crashes this compiler's inliner).
+template <typename PT, int CC>
+__device__ __noinline__ void dw_reduce_block_call(const PT* __restrict__ part, int64_t P, int32_t H,
+                                                  float* __restrict__ dw, int64_t blk, double* sm_red) {
+    dw_reduce_block<PT, CC>(part, P, H, dw, nullptr, H, blk, sm_red);
+}
+
+// Several deferred reductions in one launch, all with partial rows of type
+// PT: job k owns the blocks [block0_k, block0_{k+1}), and each of its blocks
+// does exactly what block (blockIdx - block0_k) of k_dw_reduce does for that
+// job alone, so every job's dw has the bits of the separate reduce.
+template <typename PT>
+__global__ void __launch_bounds__(kReduceThreads) k_dw_reduce_batch(DwJobs jobs) {
+    __shared__ double sm_red[(kReduceThreads / 64) * kReduceChunks * (16 / sizeof(PT))];
+    const int64_t b = blockIdx.x;
+    // the block's job, read field by field in a uniform loop (no dynamic
+    // index into the argument table)
+    const void* part = nullptr;
+    int64_t P = 0, block0 = 0;
+    int32_t H = 0;
+    float* dw = nullptr;
+#pragma unroll
+    for (int i = 0; i < kMaxBatchJobs; ++i) {
+        if (i < jobs.n && b >= jobs.j[i].block0) {
+            part = jobs.j[i].part;
+            P = jobs.j[i].P;
+            H = jobs.j[i].H;
+            dw = jobs.j[i].dw;
+            block0 = jobs.j[i].block0;
+        }
+    }
+    dw_reduce_block_call<PT, kReduceChunks>(static_cast<const PT*>(part), P, H, dw, b - block0, sm_red);
 }
 
 // Zero fill with vector stores (used for workspace initialisation; a kernel
@@ -110,6 +152,17 @@ int launch_col_reduce(const void* partial, const Route& rt, int32_t W, float* ou
         launch_kernel((k_dw_reduce<float, kReduceChunks>), grid, block, lds, s,
                       static_cast<const float*>(partial), (int64_t)rt.r.partials, W, out0, out1,
                       split);
+    return hipGetLastError() == hipSuccess ? RMSN_OK : RMSN_ERR_LAUNCH;
+}
+
+int launch_dw_reduce_batch(const DwJobs& jobs, int64_t blocks, hipStream_t s) {
+    if (jobs.n < 1 || blocks < 1) return RMSN_OK;
+    if (jobs.j[0].f64)
+        launch_kernel(k_dw_reduce_batch<double>, dim3((unsigned)blocks), dim3((unsigned)kReduceThreads),
+                      0, s, jobs);
+    else
+        launch_kernel(k_dw_reduce_batch<float>, dim3((unsigned)blocks), dim3((unsigned)kReduceThreads),
+                      0, s, jobs);
     return hipGetLastError() == hipSuccess ? RMSN_OK : RMSN_ERR_LAUNCH;
 }
 

@@ -75,6 +75,24 @@ struct BwdParams {
     float eps;              // recompute form only
 };
 
+// One deferred dw reduction of a batch: the partial rows an earlier
+// backward left (P rows of H, FP64 if f64 else FP32), its dw, and the first
+// block of the batched launch that works on it.
+struct DwJob {
+    const void* part;
+    int64_t P;
+    int32_t H;
+    int32_t f64;
+    float* dw;
+    int64_t block0;
+};
+// Jobs per batched launch (the table travels in the kernel arguments).
+constexpr int kMaxBatchJobs = 32;
+struct DwJobs {
+    int32_t n;
+    DwJob j[kMaxBatchJobs];
+};
+
 // LayerNorm (contiguous [rows, H]).
 struct LnFwdParams {
     const uint16_t* x;
@@ -124,6 +142,7 @@ int launch_fwd(const FwdParams& p, const Route& rt, rmsn_dtype_t wdt, bool resid
 int launch_bwd_row(const BwdParams& p, const Route& rt, rmsn_dtype_t wdt, int form,
                    hipStream_t s);
 int launch_dw_reduce(const BwdParams& p, const Route& rt, hipStream_t s);
+int launch_dw_reduce_batch(const DwJobs& jobs, int64_t blocks, hipStream_t s);
 // Column reduce of rt.partials partial rows of W columns: columns < split go
 // to out0, the rest to out1.
 int launch_col_reduce(const void* partial, const Route& rt, int32_t W, float* out0, float* out1,

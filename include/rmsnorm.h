@@ -216,6 +216,61 @@ int rmsnorm_residual_bwd_strided(const void* dy, rmsn_view_t dyv, const void* h,
                                  rmsn_view_t dhv, float* dw, void* workspace,
                                  size_t workspace_bytes, hipStream_t stream);
 
+/* ------------------------------------------- deferred dw reduction
+ *
+ * The deterministic backward is a row kernel that leaves per-block partial
+ * rows of dw, then a fixed-order reduce of those rows into dw (the pages'
+ * "chunk-partials pair": flashinfer PR "fix(cake_rmsnorm): sm_100a and
+ * sm_107a dw-accuracy backward routes", "Changed windows by reason"). A
+ * training step needs dw only at the optimizer, after the whole backward, so
+ * these calls split the pair: each norm's backward leaves its partial rows in
+ * a caller buffer, and one rmsnorm_dw_reduce_batch call later reduces the
+ * partials of many norms in one launch. Each job's dw then has exactly the
+ * bits rmsnorm_bwd_strided (or rmsnorm_residual_bwd_strided) returns in
+ * deterministic mode for the same call; dx (dh) is the same as there too.
+ */
+
+/* Bytes of the partial-rows buffer a deferred backward of `rows` rows of H
+ * needs (0 for an invalid shape). The layout is a function of (rows, H) and
+ * the route table: keep route overrides unchanged between the backward and
+ * its reduce. */
+size_t rmsnorm_bwd_partials_bytes(int64_t rows, int64_t H, rmsn_dtype_t w_dtype);
+
+/* rmsnorm_bwd_strided (deterministic) without its dw reduction: dx is
+ * written, and the dw partial rows are left in `partials` (256-byte
+ * aligned, at least rmsnorm_bwd_partials_bytes bytes, owned by the caller
+ * until the reduce has run). */
+int rmsnorm_bwd_strided_partials(const void* dy, rmsn_view_t dyv, const void* x, rmsn_view_t xv,
+                                 const float* rstd, const void* w, rmsn_dtype_t w_dtype, void* dx,
+                                 rmsn_view_t dxv, void* partials, size_t partials_bytes,
+                                 hipStream_t stream);
+
+/* rmsnorm_residual_bwd_strided (deterministic) without its dw reduction; the
+ * partials as above. */
+int rmsnorm_residual_bwd_strided_partials(const void* dy, rmsn_view_t dyv, const void* h,
+                                          rmsn_view_t hv, const void* dres, rmsn_view_t dresv,
+                                          const float* rstd, const void* w, rmsn_dtype_t w_dtype,
+                                          void* dh, rmsn_view_t dhv, void* partials,
+                                          size_t partials_bytes, hipStream_t stream);
+
+/* One deferred reduction: the partial rows of one earlier call (rows = its
+ * T*heads, H and w_dtype as passed to it) and the dw [H] FP32 to write. */
+typedef struct {
+    const void* partials;
+    size_t partials_bytes;
+    int64_t rows;
+    int64_t H;
+    rmsn_dtype_t w_dtype;
+    float* dw;
+} rmsn_dw_job_t;
+
+/* Reduce n deferred jobs into their dw on `stream`, in as few launches as
+ * the job table allows (one per 32 jobs of each partial precision). Every
+ * job is checked before anything is enqueued: a buffer smaller than its
+ * layout needs is RMSN_ERR_WORKSPACE, a dw overlapping any job's partials or
+ * another dw is RMSN_ERR_ALIAS. n == 0 does nothing. */
+int rmsnorm_dw_reduce_batch(const rmsn_dw_job_t* jobs, int n, hipStream_t stream);
+
 /* -------------------------------------------------------------- LayerNorm
  *
  * The adjacent normalisation of the same training stacks (ROCm

@@ -110,6 +110,57 @@ int main() {
     EXPECT(rmsnorm_workspace_init(WS, need, s), RMSN_ERR_LAUNCH);
     EXPECT(rmsnorm_workspace_init(nullptr, 16, s), RMSN_ERR_NULL);
 
+    // deferred dw reduction
+    const rmsn_view_t pv = {T, 1, H, H, 0};
+    const size_t pneed = rmsnorm_bwd_partials_bytes(T, H, RMSN_BF16);
+    if (pneed == 0 || rmsnorm_bwd_partials_bytes(T, 7, RMSN_BF16) != 0) ++g_fail;
+    EXPECT(rmsnorm_bwd_strided_partials(DY, pv, X, pv, rs, W, RMSN_BF16, DX, pv, WS, pneed, s),
+           RMSN_ERR_LAUNCH);
+    EXPECT(rmsnorm_bwd_strided_partials(DY, pv, X, pv, rs, W, RMSN_BF16, DX, pv, WS, pneed - 1, s),
+           RMSN_ERR_WORKSPACE);
+    EXPECT(rmsnorm_bwd_strided_partials(DY, pv, X, pv, rs, W, RMSN_BF16, DX, pv, fake(A + 7 * G + 16),
+                                        pneed, s), RMSN_ERR_WORKSPACE);
+    EXPECT(rmsnorm_bwd_strided_partials(DY, pv, X, pv, rs, W, RMSN_BF16, DX, pv, DX, pneed, s),
+           RMSN_ERR_ALIAS);
+    EXPECT(rmsnorm_residual_bwd_strided_partials(DY, pv, X, pv, R, pv, rs, W, RMSN_BF16, DX, pv, WS,
+                                                 pneed, s), RMSN_ERR_LAUNCH);
+    {
+        const rmsn_view_t small = {64, 1, 256, 256, 0}, none = {0, 1, 256, 256, 0};
+        const size_t sneed = rmsnorm_bwd_partials_bytes(64, 256, RMSN_F32);
+        EXPECT(rmsnorm_bwd_strided_partials(DY, small, X, small, rs, W, RMSN_F32, DX, small, WS,
+                                            sneed, s), RMSN_ERR_LAUNCH);
+        EXPECT(rmsnorm_bwd_strided_partials(DY, none, X, none, rs, W, RMSN_F32, DX, none, WS, sneed, s),
+               RMSN_ERR_LAUNCH);  // zero rows: the fill of one zero partial row
+    }
+    rmsn_dw_job_t jobs[40];
+    for (int i = 0; i < 40; ++i)
+        jobs[i] = rmsn_dw_job_t{fake(A + 7 * G + (uintptr_t)i * (pneed + 256)), pneed, T, H, RMSN_BF16,
+                                static_cast<float*>(fake(A + 6 * G + (uintptr_t)i * H * 4))};
+    EXPECT(rmsnorm_dw_reduce_batch(jobs, 40, s), RMSN_ERR_LAUNCH);
+    EXPECT(rmsnorm_dw_reduce_batch(jobs, 0, s), RMSN_OK);
+    EXPECT(rmsnorm_dw_reduce_batch(nullptr, 1, s), RMSN_ERR_NULL);
+    EXPECT(rmsnorm_dw_reduce_batch(jobs, -1, s), RMSN_ERR_SHAPE);
+    {
+        rmsn_dw_job_t bad[2] = {jobs[0], jobs[1]};
+        bad[1].partials_bytes = pneed / 2;
+        EXPECT(rmsnorm_dw_reduce_batch(bad, 2, s), RMSN_ERR_WORKSPACE);
+        bad[1] = jobs[1];
+        bad[1].dw = bad[0].dw;  // two jobs write one dw
+        EXPECT(rmsnorm_dw_reduce_batch(bad, 2, s), RMSN_ERR_ALIAS);
+        bad[1] = jobs[1];
+        bad[1].dw = static_cast<float*>(const_cast<void*>(bad[0].partials));  // dw over partials
+        EXPECT(rmsnorm_dw_reduce_batch(bad, 2, s), RMSN_ERR_ALIAS);
+        bad[1] = jobs[1];
+        bad[1].H = 12;
+        EXPECT(rmsnorm_dw_reduce_batch(bad, 2, s), RMSN_ERR_SHAPE);
+        bad[1] = jobs[1];
+        bad[1].w_dtype = (rmsn_dtype_t)3;
+        EXPECT(rmsnorm_dw_reduce_batch(bad, 2, s), RMSN_ERR_DTYPE);
+        bad[1] = jobs[1];
+        bad[1].partials = fake(A + 7 * G + 8);
+        EXPECT(rmsnorm_dw_reduce_batch(bad, 2, s), RMSN_ERR_ALIGN);
+    }
+
     // LayerNorm
     const size_t lneed = layernorm_bwd_workspace_bytes(T, H, RMSN_BF16, 1);
     EXPECT(layernorm_fwd(X, W, R, RMSN_BF16, 1e-5f, Y, mu, rs, T, H, s), RMSN_ERR_LAUNCH);

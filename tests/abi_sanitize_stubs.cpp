@@ -15,4 +15,5 @@ int launch_ln_fwd(const LnFwdParams&, const Route&, rmsn_dtype_t, hipStream_t) {
 int launch_ln_bwd_row(const LnBwdParams&, const Route&, rmsn_dtype_t, hipStream_t) { return RMSN_ERR_LAUNCH; }
 int launch_bwd_small(const BwdParams&, const Route&, rmsn_dtype_t, bool, hipStream_t) { return RMSN_ERR_LAUNCH; }
 int launch_fill_zero(void*, size_t, hipStream_t) { return RMSN_ERR_LAUNCH; }
+int launch_dw_reduce_batch(const DwJobs&, int64_t, hipStream_t) { return RMSN_ERR_LAUNCH; }
 }  // namespace rmsn
