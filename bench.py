@@ -25,6 +25,11 @@ checkpointed step: forward, forward recompute, backward):
   fwd+bwd_recompute    forward, then the backward that recomputes rstd from
                        x itself (plain forms): the checkpointed step with the
                        recompute forward folded into the backward
+  fwd+bwd_deferred     forward, then the backward that leaves its dw partial
+                       rows; the K steps of a replay end with one batched
+                       reduce of their K dw (a model whose layers' dw are
+                       reduced together at the end of the backward). Not the
+                       metric's step: reported beside it, in per_config
 
 Timing (the pages' protocol, Cake page "Measurement", on HIP graphs):
 * a replay is one HIP graph holding K = --steps steps; its GPU span is
@@ -80,7 +85,7 @@ FLUSH_BYTES = 512 << 20
 METRIC = "RMSNorm fwd+bwd effective HBM GB/s and % of 8 TB/s peak, per (T,H)"
 DEFAULT_CONFIG = "c3_T131072_H2048_f32w_heavy"
 DEFAULT_LN_CONFIG = "ln_T8192_H4096_bf16w"
-OPS = ("fwd+bwd", "fwd", "bwd", "2xfwd+bwd", "fwd+bwd_recompute")
+OPS = ("fwd+bwd", "fwd", "bwd", "2xfwd+bwd", "fwd+bwd_recompute", "fwd+bwd_deferred")
 P = ctypes.c_void_p
 
 
@@ -129,7 +134,8 @@ class Work:
         self.__dict__.update(kw)
 
     def n_fwd(self, op):
-        return {"fwd+bwd": 1, "fwd": 1, "bwd": 0, "2xfwd+bwd": 2, "fwd+bwd_recompute": 1}[op]
+        return {"fwd+bwd": 1, "fwd": 1, "bwd": 0, "2xfwd+bwd": 2, "fwd+bwd_recompute": 1,
+                "fwd+bwd_deferred": 1}[op]
 
     def step_bytes(self, op):
         fwd_b, _, bwd_b = self.bytes
@@ -230,9 +236,37 @@ def prepare_rmsnorm(name, seed, torch, np, synth, _lib, lib, dev):
                                                P(s["dx"].data_ptr()), dxv, P(s["dw"].data_ptr()),
                                                wsp, nb, stream))
 
+    def deferred_slots(K):
+        """K partial-row buffers and dw outputs, one per step of a replay, and
+        the job table of their one batched reduce."""
+        need = lib.rmsnorm_bwd_partials_bytes(rows, H, wdt)
+        slots = []
+        for _ in range(K):
+            raw = torch.empty(need + 256, dtype=torch.uint8, device=dev)
+            slots.append(dict(raw=raw, ptr=raw.data_ptr() + (-raw.data_ptr()) % 256, nb=need,
+                              dw=torch.empty(H, dtype=torch.float32, device=dev)))
+        jobs = (_lib.DwJob * K)(*[_lib.DwJob(sl["ptr"], sl["nb"], rows, H, wdt, sl["dw"].data_ptr())
+                                  for sl in slots])
+        return dict(slots=slots, jobs=jobs, n=K)
+
+    def bwd_partial(s, slot, stream):
+        if residual:
+            _lib.check(lib.rmsnorm_residual_bwd_strided_partials(
+                P(s["dy"].data_ptr()), cv, P(s["h"].data_ptr()), cv,
+                P(s["dres"].data_ptr()) if with_dres else None, cv, P(s["rstd"].data_ptr()),
+                P(w.data_ptr()), wdt, P(s["dx"].data_ptr()), cv, P(slot["ptr"]), slot["nb"], stream))
+        else:
+            _lib.check(lib.rmsnorm_bwd_strided_partials(
+                P(s["dy"].data_ptr()), cv, P(s["x"].data_ptr()), xv, P(s["rstd"].data_ptr()),
+                P(w.data_ptr()), wdt, P(s["dx"].data_ptr()), dxv, P(slot["ptr"]), slot["nb"], stream))
+
+    def reduce_slots(d, stream):
+        _lib.check(lib.rmsnorm_dw_reduce_batch(d["jobs"], d["n"], stream))
+
     return Work(name=name, norm="rmsnorm", wl=wl, rows=rows, T=T, heads=heads, H=H,
                 residual=residual, with_dres=with_dres, wdtype=wl.w.dtype, sets=sets, ws=ws,
-                fwd=fwd, bwd=bwd, out_keys=("y", "dx", "dw"),
+                fwd=fwd, bwd=bwd, out_keys=("y", "dx", "dw"), deferred_slots=deferred_slots,
+                bwd_partial=bwd_partial, reduce_slots=reduce_slots,
                 bytes=algorithmic_bytes(rows, H, sw, residual, with_dres))
 
 
@@ -300,18 +334,44 @@ def measure_op(args, torch, rn, _lib, dev, wk, op, nondet=True):
     K, W = args.steps, args.warmup
     cur = torch.cuda.current_stream(dev)
     sp = P(cur.cuda_stream)
-    step = wk.step_fn(op)
+    deferred = op == "fwd+bwd_deferred"
+    step = None if deferred else wk.step_fn(op)
+    dslots = wk.deferred_slots(K) if deferred else None
     has_bwd = op != "fwd"
     out_keys = [k for k in wk.out_keys if (k == "y" and wk.n_fwd(op)) or (k != "y" and has_bwd)]
+
+    def run(i0, n, det, stream):
+        """Steps i0 .. i0 + n - 1. Deferred: n is a multiple of K, and each K
+        steps (forward, backward leaving its partial rows in slot k) end with
+        the one batched reduce of their K dw."""
+        if not deferred:
+            for i in range(i0, i0 + n):
+                step(sets[i % n_sets], det, stream)
+            return
+        for g0 in range(i0, i0 + n, K):
+            for k in range(K):
+                s = sets[(g0 + k) % n_sets]
+                wk.fwd(s, stream)
+                wk.bwd_partial(s, dslots["slots"][k], stream)
+            wk.reduce_slots(dslots, stream)
+
+    def outputs():
+        o = {k: sets[0][k] for k in out_keys}
+        if deferred:
+            o["dw"] = dslots["slots"][0]["dw"]
+        return o
 
     # every set gets a forward's rstd (and h) first, so a backward-only step
     # has its inputs; then the eager warm-up and a reference result for set 0
     for s in sets:
         wk.fwd(s, sp)
-    for i in range(max(1, W)):  # at least one step: set 0's outputs are the reference
-        step(sets[i % n_sets], 1, sp)
+    if deferred:
+        for _ in range(max(1, math.ceil(W / K))):
+            run(0, K, 1, sp)
+    else:
+        run(0, max(1, W), 1, sp)  # at least one step: set 0's outputs are the reference
     torch.cuda.synchronize()
-    ref = {k: sets[0][k].clone() for k in out_keys}
+    ref = {k: t.clone() for k, t in outputs().items()}
 
     def capture(det: int):
         g = torch.cuda.CUDAGraph()
@@ -320,23 +380,22 @@ def measure_op(args, torch, rn, _lib, dev, wk, op, nondet=True):
         with torch.cuda.stream(cs):
             with torch.cuda.graph(g, stream=cs):
                 csp = P(torch.cuda.current_stream(dev).cuda_stream)
-                for i in range(K):
-                    step(sets[i % n_sets], det, csp)
+                run(0, K, det, csp)
         torch.cuda.synchronize()
         return g
 
     graphs = [("det", capture(1)), ("det_aa", capture(1))]
-    if nondet and has_bwd:
+    if nondet and has_bwd and not deferred:
         graphs.append(("nondet", capture(0)))
 
     def check(g, tag):
-        for k in out_keys:
-            sets[0][k].zero_()
+        for t in outputs().values():
+            t.zero_()
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
-        for k in out_keys:
-            assert same_bits(torch, sets[0][k], ref[k]), f"{wk.name} {op} {tag}: graph {k} != eager"
+        for k, t in outputs().items():
+            assert same_bits(torch, t, ref[k]), f"{wk.name} {op} {tag}: graph {k} != eager"
 
     rounds = max(1, args.rounds)
     per_round = max(1, math.ceil(args.replays / rounds))
@@ -375,16 +434,16 @@ def measure_op(args, torch, rn, _lib, dev, wk, op, nondet=True):
     step_ms = st["det"]["median"]
     k_warm = int(min(1000, max(10, K, math.ceil(25.0 / max(step_ms, 1e-3)))))
     k_timed = max(40, K)
+    if deferred:  # whole groups of K steps
+        k_warm, k_timed = K * math.ceil(k_warm / K), K * math.ceil(k_timed / K)
     rn.rmsnorm_timing_read()
     rn.rmsnorm_timing_enable(False)
     torch.cuda.synchronize()
     torch.cuda._sleep(int(2e8))
     t0 = time.perf_counter()
-    for i in range(k_warm):
-        step(sets[i % n_sets], 1, sp)
+    run(0, k_warm, 1, sp)
     rn.rmsnorm_timing_enable(True)
-    for i in range(k_warm, k_warm + k_timed):
-        step(sets[i % n_sets], 1, sp)
+    run(k_warm, k_timed, 1, sp)
     t_issue = time.perf_counter() - t0
     torch.cuda.synchronize()
     timers = rn.rmsnorm_timing_read()
@@ -657,7 +716,7 @@ def main() -> int:
         progress(f"{args.config} bwd alone: timing (cold backward)")
         cold = measure_op(args, torch, rn, _lib, dev, wk, "bwd", nondet=False)
     flush_m = None
-    if not args.no_flush_check:
+    if not args.no_flush_check and op != "fwd+bwd_deferred":
         progress(f"{args.config} {op}: flush-protocol cross-check")
         flush_m = measure_flush(args, torch, dev, wk, op)
     dom_name, dom_bytes, dom_us = dominant(wk, op, m)
@@ -695,7 +754,8 @@ def main() -> int:
             progress(f"per-config {name}: generating inputs")
             w2 = prepare(name, args.seed, torch, np, synth, _lib, lib, dev)
             entry = per_config.setdefault(name, {})
-            for o in ("fwd+bwd", "bwd", "fwd", "2xfwd+bwd"):
+            ops = ("fwd+bwd", "bwd", "fwd", "2xfwd+bwd") + (() if ln else ("fwd+bwd_deferred",))
+            for o in ops:
                 if o in entry:
                     continue
                 progress(f"per-config {name} {o}: timing")

@@ -93,14 +93,6 @@ __global__ void __launch_bounds__(kReduceThreads) k_dw_reduce(const PT* __restri
     dw_reduce_block<PT, CC>(part, P, H, dw, out1, split, (int64_t)blockIdx.x, sm_red);
 }
 
-// The same block body behind a call (the batched kernel calls it: inlining
-// it there crashes this compiler's inliner).
-template <typename PT, int CC>
-__device__ __noinline__ void dw_reduce_block_call(const PT* __restrict__ part, int64_t P, int32_t H,
-                                                  float* __restrict__ dw, int64_t blk, double* sm_red) {
-    dw_reduce_block<PT, CC>(part, P, H, dw, nullptr, H, blk, sm_red);
-}
-
 // Several deferred reductions in one launch, all with partial rows of type
 // PT: job k owns the blocks [block0_k, block0_{k+1}), and each of its blocks
 // does exactly what block (blockIdx - block0_k) of k_dw_reduce does for that
@@ -125,7 +117,17 @@ __global__ void __launch_bounds__(kReduceThreads) k_dw_reduce_batch(DwJobs jobs)
             block0 = jobs.j[i].block0;
         }
     }
-    dw_reduce_block_call<PT, kReduceChunks>(static_cast<const PT*>(part), P, H, dw, b - block0, sm_red);
+    // the job's pointers are uniform across the block: passed through
+    // readfirstlane they reach the inlined body as plain values (inlining it
+    // on the argument table's own pointers crashes this compiler's inliner)
+    const uint64_t pb = (uint64_t)part, db = (uint64_t)dw;
+    const PT* part_u = reinterpret_cast<const PT*>(
+        ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(pb >> 32)) << 32) |
+        (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)pb));
+    float* dw_u = reinterpret_cast<float*>(
+        ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(db >> 32)) << 32) |
+        (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)db));
+    dw_reduce_block<PT, kReduceChunks>(part_u, P, H, dw_u, nullptr, H, b - block0, sm_red);
 }
 
 // Zero fill with vector stores (used for workspace initialisation; a kernel
