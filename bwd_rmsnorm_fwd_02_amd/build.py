@@ -15,7 +15,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libbwd_rmsnorm.so")
-SOURCES = ["fwd_bf16w.hip", "fwd_f32w.hip", "bwd_bf16w.hip", "bwd_f32w.hip", "ln_bf16w.hip",
+SOURCES = ["fwd_bf16w.hip", "fwd_f32w.hip", "bwd_bf16w.hip", "bwd_f32w.hip", "bwd_bf16w_ca.hip",
+           "bwd_f32w_ca.hip", "ln_bf16w.hip",
            "ln_f32w.hip", "reduce.hip", "route.cpp", "api.cpp", "noalloc.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

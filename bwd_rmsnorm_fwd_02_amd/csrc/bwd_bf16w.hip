@@ -4,7 +4,7 @@
 namespace rmsn {
 
 int launch_bwd_row_bf16w(const BwdParams& p, const Route& rt, int form, hipStream_t s) {
-    return launch_bwd_row_wt<uint16_t>(p, rt, form, s);
+    return launch_bwd_row_wt<uint16_t, false>(p, rt, form, s);
 }
 
 int launch_bwd_small_bf16w(const BwdParams& p, const Route& rt, bool residual, hipStream_t s) {

@@ -282,7 +282,8 @@ __device__ __forceinline__ void load_weights(const BwdParams& p, int slot, int l
 // Large-T row kernel: dx for the block's rows plus the block's dw sums.
 // Each iteration a row group takes U rows; with U <= 2 the next iteration's
 // rows are loaded before the current ones are processed.
-template <int NV, int U, typename WT, bool RES, bool WIDE, int MODE, bool RC = false, int NT = 0>
+template <int NV, int U, typename WT, bool RES, bool WIDE, int MODE, bool RC = false, int NT = 0,
+          bool CA = false>
 __global__ void __launch_bounds__(WIDE ? (NV * U >= 4 ? 512 : 1024) : 256) k_bwd_row(BwdParams p) {
     // Rows above 8192 elements take four vectors per lane on 512 lanes (a
     // 1024-lane group leaves 128 registers per lane); with the row unpacked
@@ -293,8 +294,10 @@ __global__ void __launch_bounds__(WIDE ? (NV * U >= 4 ? 512 : 1024) : 256) k_bwd
     const int tid = threadIdx.x;
     const int slot = tid / p.tpr;
     const int lr = tid - slot * p.tpr;
-    // LDS: [H] doubles for the slot combine, then (recompute form) the FP64
-    // exchange area, then the FP32 row-sum exchange area
+    // LDS: [H] doubles for the serial slot combine, then (recompute form)
+    // the FP64 exchange area, then the FP32 row-sum exchange area. The
+    // one-step combine (CA) takes [rpb, H] doubles from the start, over the
+    // exchange areas, once the loop is done with them.
     double* comb = lds_bwd;
     double* redd = lds_bwd + (p.rpb > 1 ? p.H : 0);
     const int nexch = WIDE ? 2 * p.rpb * U * (p.tpr >> 6) : 0;
@@ -346,6 +349,47 @@ __global__ void __launch_bounds__(WIDE ? (NV * U >= 4 ? 512 : 1024) : 256) k_bwd
     }
 
     // Combine the row slots in slot order: acc(0) + acc(1) + ... (fixed).
+    if constexpr (CA && (MODE == kModePartF64 || MODE == kModePartF32)) {
+        // Every slot stores its sums at once; then each thread folds
+        // whole columns in slot order (the same additions as the serial
+        // form below) and writes them to the block's partial row.
+        __syncthreads();
+        if (slot < p.rpb) {
+#pragma unroll
+            for (int v = 0; v < NV; ++v)
+                if (vok[v])
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        comb[(int64_t)slot * p.H + (lr + v * p.tpr) * kVec + e] = acc[v][e];
+        }
+        __syncthreads();
+        // a thread takes column pairs; the reads of four slots are issued
+        // before their sums
+        const int npair = p.H >> 1;
+        for (int i = tid; i < npair; i += (int)blockDim.x) {
+            const double2* cp = reinterpret_cast<const double2*>(comb) + i;
+            double2 sum = cp[0];
+            int q = 1;
+            for (; q + 4 <= p.rpb; q += 4) {
+                const double2 a0 = cp[(int64_t)q * npair], a1 = cp[(int64_t)(q + 1) * npair];
+                const double2 a2 = cp[(int64_t)(q + 2) * npair], a3 = cp[(int64_t)(q + 3) * npair];
+                sum.x += a0.x; sum.y += a0.y;
+                sum.x += a1.x; sum.y += a1.y;
+                sum.x += a2.x; sum.y += a2.y;
+                sum.x += a3.x; sum.y += a3.y;
+            }
+            for (; q < p.rpb; ++q) {
+                const double2 a = cp[(int64_t)q * npair];
+                sum.x += a.x; sum.y += a.y;
+            }
+            if constexpr (MODE == kModePartF64)
+                reinterpret_cast<double2*>(static_cast<double*>(p.partial) + b * p.H)[i] = sum;
+            else
+                reinterpret_cast<float2*>(static_cast<float*>(p.partial) + b * p.H)[i] =
+                    make_float2((float)sum.x, (float)sum.y);
+        }
+        return;
+    }
     if (p.rpb > 1) {
         for (int s = 1; s < p.rpb; ++s) {
             __syncthreads();
@@ -479,6 +523,9 @@ __global__ void __launch_bounds__(256) k_bwd_small(BwdParams p) {
 
 // ----------------------------------------------------------------- launchers
 
+// LDS of the row kernel: the serial combine's [H] doubles (several slots)
+// and the loop's row-sum exchange after them; the one-step combine reuses
+// the whole area and extends it to [rpb, H] doubles.
 inline size_t bwd_row_lds_bytes(const rmsn_route_t& r, int H, bool rc) {
     size_t lds = r.rows_per_block > 1 ? sizeof(double) * (size_t)H : 0;
     if (r.lanes_per_row > 64) {
@@ -486,59 +533,66 @@ inline size_t bwd_row_lds_bytes(const rmsn_route_t& r, int H, bool rc) {
         lds += sizeof(float) * n;
         if (rc) lds += sizeof(double) * n;
     }
+    if (bwd_row_comb_all(r, H)) {
+        const size_t all = sizeof(double) * (size_t)r.rows_per_block * (size_t)H;
+        if (all > lds) lds = all;
+    }
     return lds;
 }
 
-template <int NV, int U, typename WT, bool RES, bool WIDE, bool RC, int NT>
+// CA: the one-step slot combine (bwd_row_comb_all), compiled as its own
+// kernels so that the serial-combine kernels keep their code unchanged.
+template <int NV, int U, typename WT, bool RES, bool WIDE, bool RC, int NT, bool CA>
 static int launch_row_nt(const BwdParams& p, const Route& rt, size_t lds, hipStream_t s) {
     dim3 grid((unsigned)rt.r.grid), block((unsigned)rt.r.block_threads);
     if (rt.r.kind == RMSN_KIND_BWD_ROW_ATOMIC) {
-        if constexpr (NV == 1 && U <= 2)
+        if constexpr (NV == 1 && U <= 2 && !CA)
             launch_kernel((k_bwd_row<NV, U, WT, RES, WIDE, kModeAtomic, RC, NT>), grid, block, lds, s, p);
         else
             return RMSN_ERR_SHAPE;
     } else if (rt.r.partial_f64) {
-        launch_kernel((k_bwd_row<NV, U, WT, RES, WIDE, kModePartF64, RC, NT>), grid, block, lds, s, p);
+        launch_kernel((k_bwd_row<NV, U, WT, RES, WIDE, kModePartF64, RC, NT, CA>), grid, block, lds, s, p);
     } else {
-        launch_kernel((k_bwd_row<NV, U, WT, RES, WIDE, kModePartF32, RC, NT>), grid, block, lds, s, p);
+        launch_kernel((k_bwd_row<NV, U, WT, RES, WIDE, kModePartF32, RC, NT, CA>), grid, block, lds, s, p);
     }
     return hipGetLastError() == hipSuccess ? RMSN_OK : RMSN_ERR_LAUNCH;
 }
 
-template <int NV, int U, typename WT, bool RES, bool WIDE, bool RC>
+template <int NV, int U, typename WT, bool RES, bool WIDE, bool RC, bool CA>
 static int launch_row_mode(const BwdParams& p, const Route& rt, size_t lds, hipStream_t s) {
     switch (rt.r.stream_loads) {
-        case 0: return launch_row_nt<NV, U, WT, RES, WIDE, RC, 0>(p, rt, lds, s);
-        case 1: return launch_row_nt<NV, U, WT, RES, WIDE, RC, 1>(p, rt, lds, s);
-        case 2: return launch_row_nt<NV, U, WT, RES, WIDE, RC, 2>(p, rt, lds, s);
+        case 0: return launch_row_nt<NV, U, WT, RES, WIDE, RC, 0, CA>(p, rt, lds, s);
+        case 1: return launch_row_nt<NV, U, WT, RES, WIDE, RC, 1, CA>(p, rt, lds, s);
+        case 2: return launch_row_nt<NV, U, WT, RES, WIDE, RC, 2, CA>(p, rt, lds, s);
         default: return RMSN_ERR_SHAPE;
     }
 }
 
-template <int NV, int U, typename WT, bool RES, bool RC>
+template <int NV, int U, typename WT, bool RES, bool RC, bool CA>
 static int launch_row_t(const BwdParams& p, const Route& rt, hipStream_t s) {
+    if (bwd_row_comb_all(rt.r, p.H) != CA) return RMSN_ERR_SHAPE;
     const size_t lds = bwd_row_lds_bytes(rt.r, p.H, RC);
-    if (rt.r.lanes_per_row > 64) return launch_row_mode<NV, U, WT, RES, true, RC>(p, rt, lds, s);
-    return launch_row_mode<NV, U, WT, RES, false, RC>(p, rt, lds, s);
+    if (rt.r.lanes_per_row > 64) return launch_row_mode<NV, U, WT, RES, true, RC, CA>(p, rt, lds, s);
+    return launch_row_mode<NV, U, WT, RES, false, RC, CA>(p, rt, lds, s);
 }
 
 // (NV, U) pairs compiled: NV * U <= 8 with NV <= 2, and NV 4 with U 1.
-template <typename WT, bool RES, bool RC>
+template <typename WT, bool RES, bool RC, bool CA>
 static int launch_row_shape(const BwdParams& p, const Route& rt, hipStream_t s) {
     const int nv = rt.r.vec_per_lane, u = rt.r.unroll;
-    if (nv == 4) return u == 1 ? launch_row_t<4, 1, WT, RES, RC>(p, rt, s) : RMSN_ERR_SHAPE;
+    if (nv == 4) return u == 1 ? launch_row_t<4, 1, WT, RES, RC, CA>(p, rt, s) : RMSN_ERR_SHAPE;
     if (nv == 1) {
         switch (u) {
-            case 1: return launch_row_t<1, 1, WT, RES, RC>(p, rt, s);
-            case 2: return launch_row_t<1, 2, WT, RES, RC>(p, rt, s);
-            case 4: return launch_row_t<1, 4, WT, RES, RC>(p, rt, s);
-            case 8: return launch_row_t<1, 8, WT, RES, RC>(p, rt, s);
+            case 1: return launch_row_t<1, 1, WT, RES, RC, CA>(p, rt, s);
+            case 2: return launch_row_t<1, 2, WT, RES, RC, CA>(p, rt, s);
+            case 4: return launch_row_t<1, 4, WT, RES, RC, CA>(p, rt, s);
+            case 8: return launch_row_t<1, 8, WT, RES, RC, CA>(p, rt, s);
         }
     } else if (nv == 2) {
         switch (u) {
-            case 1: return launch_row_t<2, 1, WT, RES, RC>(p, rt, s);
-            case 2: return launch_row_t<2, 2, WT, RES, RC>(p, rt, s);
-            case 4: return launch_row_t<2, 4, WT, RES, RC>(p, rt, s);
+            case 1: return launch_row_t<2, 1, WT, RES, RC, CA>(p, rt, s);
+            case 2: return launch_row_t<2, 2, WT, RES, RC, CA>(p, rt, s);
+            case 4: return launch_row_t<2, 4, WT, RES, RC, CA>(p, rt, s);
         }
     }
     return RMSN_ERR_SHAPE;
@@ -568,12 +622,12 @@ static int launch_small_shape(const BwdParams& p, const Route& rt, hipStream_t s
 }
 
 // form: kFormPlain, kFormResidual or kFormRecompute.
-template <typename WT>
+template <typename WT, bool CA>
 static int launch_bwd_row_wt(const BwdParams& p, const Route& rt, int form, hipStream_t s) {
     switch (form) {
-        case kFormPlain: return launch_row_shape<WT, false, false>(p, rt, s);
-        case kFormResidual: return launch_row_shape<WT, true, false>(p, rt, s);
-        case kFormRecompute: return launch_row_shape<WT, false, true>(p, rt, s);
+        case kFormPlain: return launch_row_shape<WT, false, false, CA>(p, rt, s);
+        case kFormResidual: return launch_row_shape<WT, true, false, CA>(p, rt, s);
+        case kFormRecompute: return launch_row_shape<WT, false, true, CA>(p, rt, s);
         default: return RMSN_ERR_SHAPE;
     }
 }

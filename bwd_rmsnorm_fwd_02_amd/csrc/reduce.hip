@@ -191,6 +191,9 @@ int launch_fwd(const FwdParams& p, const Route& rt, rmsn_dtype_t wdt, bool resid
 
 int launch_bwd_row(const BwdParams& p, const Route& rt, rmsn_dtype_t wdt, int form,
                    hipStream_t s) {
+    if (bwd_row_comb_all(rt.r, p.H))
+        return wdt == RMSN_BF16 ? launch_bwd_row_bf16w_ca(p, rt, form, s)
+                                : launch_bwd_row_f32w_ca(p, rt, form, s);
     return wdt == RMSN_BF16 ? launch_bwd_row_bf16w(p, rt, form, s)
                             : launch_bwd_row_f32w(p, rt, form, s);
 }

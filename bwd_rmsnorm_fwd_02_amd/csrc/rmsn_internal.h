@@ -161,8 +161,25 @@ int launch_fwd_bf16w(const FwdParams& p, const Route& rt, bool residual, hipStre
 int launch_fwd_f32w(const FwdParams& p, const Route& rt, bool residual, hipStream_t s);
 int launch_bwd_row_bf16w(const BwdParams& p, const Route& rt, int form, hipStream_t s);
 int launch_bwd_row_f32w(const BwdParams& p, const Route& rt, int form, hipStream_t s);
+// The same with the one-step slot combine (bwd_row_comb_all true).
+int launch_bwd_row_bf16w_ca(const BwdParams& p, const Route& rt, int form, hipStream_t s);
+int launch_bwd_row_f32w_ca(const BwdParams& p, const Route& rt, int form, hipStream_t s);
 int launch_bwd_small_bf16w(const BwdParams& p, const Route& rt, bool residual, hipStream_t s);
 int launch_bwd_small_f32w(const BwdParams& p, const Route& rt, bool residual, hipStream_t s);
+
+// The backward row kernel combines its row slots' dw sums in one step
+// (every slot's sums in LDS at once, [rpb, H] doubles, then every thread
+// folds whole columns in slot order) when there are at least four slots and
+// the sums fit in kCombAllLds; otherwise slot by slot through an [H] area.
+// Both add in the same order. With two slots the serial form is one round
+// and measured faster (4096 x 4096: 35.9 against 36.2 us per step); with
+// eight it is seven rounds (32768 x 4 x 256: the one-step form -2.6 %).
+constexpr size_t kCombAllLds = 64 * 1024;
+
+inline bool bwd_row_comb_all(const rmsn_route_t& r, int H) {
+    return r.rows_per_block >= 4 && r.kind == RMSN_KIND_BWD_ROW_DET &&
+           sizeof(double) * (size_t)r.rows_per_block * (size_t)H <= kCombAllLds;
+}
 
 // Kernel timing hooks (api.cpp). timer_begin names the kernel kind the API
 // is about to launch; when timing is enabled, the next launch takes a pair

@@ -115,7 +115,7 @@ constexpr Entry kFwdTable[] = {
     {1 << 30, 4, 1, 0, 1},  // H <= 16384
 };
 constexpr Entry kBwdTable[] = {
-    {32, 2, 1, 128, 4},     // H <= 256: 16 lanes per row, 8 rows per block, 4 blocks per CU
+    {32, 2, 1, 256, 2},     // H <= 256: 16 lanes per row, 16 rows per block, 2 blocks per CU
     {64, 2, 2, 256, 1},     // H <= 512: 32 lanes per row, 8 row groups, 2 rows per iteration
     {192, 1, 1, 768, 1},    // H <= 1536: one lane per vector, 768-thread blocks
     {256, 1, 1, 1024, 1},   // H <= 2048: 4 row groups of 256 lanes, 1 block per CU
@@ -133,7 +133,7 @@ constexpr Entry kBwdTable[] = {
 // have, so it wants more rows in flight per CU: more vectors per lane,
 // smaller blocks, more of them.
 constexpr Entry kRcBwdTable[] = {
-    {32, 2, 1, 128, 4},     // H <= 256: as the plain backward
+    {32, 2, 1, 256, 2},     // H <= 256: as the plain backward
     {64, 4, 1, 64, 4},      // H <= 512: 16 lanes per row, 4 rows per block
     {192, 2, 2, 128, 4},    // H <= 1536: 128 lanes, 2 rows per iteration, 4 blocks per CU
     {256, 2, 2, 256, 2},    // H <= 2048: 2 row groups of 128 lanes, 2 blocks per CU

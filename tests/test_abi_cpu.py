@@ -231,7 +231,7 @@ def test_route_recompute_form_has_its_own_launch_shapes():
             (65536, 5120): (4, 1, 192, 2, 256), (1048576, 512): (4, 1, 16, 4, 1024),
             (262144, 1536): (2, 2, 128, 1, 1024), (16384, 6144): (4, 1, 192, 1, 512),
             (8192, 8192): (4, 1, 256, 1, 512), (8192, 16384): (4, 1, 512, 1, 256),
-            (786432, 256): (2, 1, 16, 8, 1024)}
+            (786432, 256): (2, 1, 16, 16, 512)}
     for (rows, H), shape in want.items():
         st, r = route(1, rows, H, 0, 1, 2)
         assert st == 0
@@ -250,8 +250,8 @@ def test_route_plain_backward_launch_shapes():
         (4096, 4096, 0, 0): (1, 1, 512, 2, 256, 0, 1),
         (131072, 2048, 1, 0): (1, 1, 256, 4, 256, 1, 2),
         (16384, 6144, 0, 1): (1, 1, 768, 1, 256, 1, 2),
-        (786432, 256, 1, 0): (2, 1, 16, 8, 1024, 1, 2),
-        (131072, 256, 1, 0): (2, 1, 16, 8, 1024, 1, 1),
+        (786432, 256, 1, 0): (2, 1, 16, 16, 512, 1, 2),
+        (131072, 256, 1, 0): (2, 1, 16, 16, 512, 1, 1),
         (1048576, 512, 0, 0): (2, 2, 32, 8, 256, 1, 2),
         (262144, 1536, 1, 0): (1, 1, 192, 4, 256, 1, 2),
         (65536, 5120, 0, 0): (4, 1, 192, 2, 256, 1, 2),
