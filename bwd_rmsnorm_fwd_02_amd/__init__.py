@@ -28,6 +28,7 @@ __all__ = [
     "rmsnorm_workspace_init", "rmsnorm_status_string", "rmsnorm_route_query",
     "rmsnorm_route_override", "rmsnorm_timing_enable", "rmsnorm_timing_read",
     "RMSNormError", "View",
+    "rms_norm", "rms_norm_residual", "layer_norm", "RMSNorm", "LayerNorm",
 ]
 
 
@@ -634,3 +635,7 @@ def rmsnorm_timing_read() -> dict:
     ms = (ctypes.c_double * n)()
     _lib.check(_lib.load().rmsnorm_timing_read(launches, ms, n))
     return {i: (int(launches[i]), float(ms[i])) for i in range(n)}
+
+
+# torch.autograd wiring of the entry points above (marshalling only)
+from .autograd import LayerNorm, RMSNorm, layer_norm, rms_norm, rms_norm_residual  # noqa: E402

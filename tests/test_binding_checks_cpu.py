@@ -143,3 +143,23 @@ def test_layernorm_checks():
     expect(ValueError, rn.layernorm_bwd, dy, x, vec(T - 1), rs, g, match="mean has")
     expect(ValueError, rn.layernorm_bwd, dy, x, mu, rs, g, dbeta=vec(H - 1), match="dbeta has")
     expect(ValueError, rn.layernorm_bwd, dy, x, mu, rs, g, dgamma=vec(H + 1), match="dgamma has")
+
+
+# ------------------------------------------------------------- autograd
+
+def test_autograd_wiring_checks():
+    """The autograd functions and modules pass their tensors to the same
+    checked entry points: a well formed call on CPU tensors stops at the
+    device check, a malformed one earlier."""
+    x, r, w = act(2, T, H), act(2, T, H), vec(H)
+    expect(TypeError, rn.rms_norm, x, w, match=DEVICE_MSG)
+    expect(TypeError, rn.rms_norm, x.float(), w, match="x must be bfloat16")
+    expect(TypeError, rn.rms_norm_residual, x, r, w, match=DEVICE_MSG)
+    expect(TypeError, rn.layer_norm, x, w, vec(H), match=DEVICE_MSG)
+    expect(TypeError, rn.RMSNorm(H), x, match=DEVICE_MSG)
+    expect(TypeError, rn.RMSNorm(H), x, r, match=DEVICE_MSG)
+    expect(TypeError, rn.LayerNorm(H, bias=False), x, match=DEVICE_MSG)
+    m = rn.RMSNorm(H, weight_dtype=BF)
+    assert m.weight.dtype == BF and m.weight.shape == (H,) and torch.all(m.weight == 1)
+    ln = rn.LayerNorm(H)
+    assert ln.bias is not None and torch.all(ln.bias == 0)
