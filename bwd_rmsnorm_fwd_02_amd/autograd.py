@@ -7,8 +7,11 @@ FP32. The forward saves its rstd (and, for LayerNorm, its mean) and hands
 it to the backward entry point, which takes the forward's row statistics.
 dw (dgamma, dbeta) comes back in FP32; autograd rounds it to the
 weight's dtype when the weight is BF16, so FP32 master weights keep all of
-it. An incoming gradient that is not contiguous (an expanded one, say) is
-copied to a contiguous tensor first.
+it. RMSNorm takes [T, H] and [T, heads, H] tensors through the strided
+entry points as they are, per-head views of a wider buffer included (rows of
+H contiguous elements, 16-byte aligned base and strides); other tensors, and
+incoming gradients that do not fit (an expanded one, say), are copied to a
+contiguous tensor first.
 
 * rms_norm(x, w) -> y.
 * rms_norm_residual(x, r, w) -> (y, h): h = BF16(x + r), the updated
@@ -29,8 +32,8 @@ from typing import Optional
 
 import torch
 
-from . import (layernorm_bwd, layernorm_fwd, rmsnorm_bwd, rmsnorm_fwd, rmsnorm_residual_bwd,
-               rmsnorm_residual_fwd)
+from . import (layernorm_bwd, layernorm_fwd, rmsnorm_bwd_strided, rmsnorm_fwd_strided,
+               rmsnorm_residual_bwd_strided, rmsnorm_residual_fwd_strided)
 
 __all__ = ["rms_norm", "rms_norm_residual", "layer_norm", "RMSNorm", "LayerNorm"]
 
@@ -40,28 +43,53 @@ def _rows(t: torch.Tensor, H: int) -> torch.Tensor:
     return t.contiguous().view(-1, H)
 
 
+def _strided_ok(t: torch.Tensor) -> bool:
+    """A [T, H] or [T, heads, H] tensor the strided entry points take as it
+    is: rows of H contiguous elements, base and strides 16-byte aligned."""
+    if t.dim() not in (2, 3) or t.stride(-1) != 1 or t.data_ptr() % 16:
+        return False
+    return all(s >= 0 and s % 8 == 0 for s in t.stride()[:-1])
+
+
+def _fit(t: torch.Tensor, shape) -> torch.Tensor:
+    """t as a tensor of `shape` ([T, H] or [T, heads, H]) that the strided
+    entry points take: t itself (or a view of it) when it fits, else a copy."""
+    v = t if tuple(t.shape) == tuple(shape) else t.reshape(shape)
+    if _strided_ok(v):
+        return v
+    v = v.contiguous()
+    return v if _strided_ok(v) else v.clone()
+
+
+def _row_shape(x: torch.Tensor):
+    """The view the entry points get: x's own [T, H] or [T, heads, H] shape
+    (per-head views of a wider buffer pass as they are), else [rows, H]."""
+    H = x.shape[-1]
+    return tuple(x.shape) if x.dim() in (2, 3) else (x.numel() // H, H)
+
+
 class _RMSNormFn(torch.autograd.Function):
     @staticmethod
     def forward(ctx, x, w, eps, deterministic):
-        H = x.shape[-1]
-        x2 = _rows(x, H)
-        y, rstd = rmsnorm_fwd(x2, w, eps)
-        ctx.save_for_backward(x2, rstd, w)
+        xs = _fit(x, _row_shape(x))
+        y, rstd = rmsnorm_fwd_strided(xs, w, eps)
+        ctx.save_for_backward(xs, rstd, w)
         ctx.deterministic = deterministic
         return y.view(x.shape)
 
     @staticmethod
     def backward(ctx, dy):
-        x2, rstd, w = ctx.saved_tensors
-        dx, dw = rmsnorm_bwd(_rows(dy, x2.shape[1]), x2, rstd, w, deterministic=ctx.deterministic)
+        xs, rstd, w = ctx.saved_tensors
+        dx, dw = rmsnorm_bwd_strided(_fit(dy, xs.shape), xs, rstd, w,
+                                     deterministic=ctx.deterministic)
         return dx.view(dy.shape), dw, None, None
 
 
 class _RMSNormResidualFn(torch.autograd.Function):
     @staticmethod
     def forward(ctx, x, r, w, eps, deterministic):
-        H = x.shape[-1]
-        h, y, rstd = rmsnorm_residual_fwd(_rows(x, H), _rows(r, H), w, eps)
+        shape = _row_shape(x)
+        h, y, rstd = rmsnorm_residual_fwd_strided(_fit(x, shape), _fit(r, shape), w, eps)
         ctx.save_for_backward(h, rstd, w)
         ctx.deterministic = deterministic
         ctx.shape = x.shape
@@ -72,10 +100,10 @@ class _RMSNormResidualFn(torch.autograd.Function):
     @staticmethod
     def backward(ctx, dy, dh_out):
         h, rstd, w = ctx.saved_tensors
-        H = h.shape[1]
-        dy2 = torch.zeros_like(h) if dy is None else _rows(dy, H)
-        dres = None if dh_out is None else _rows(dh_out, H)
-        dh, dw = rmsnorm_residual_bwd(dy2, h, rstd, w, dres=dres, deterministic=ctx.deterministic)
+        dys = torch.zeros_like(h) if dy is None else _fit(dy, h.shape)
+        dres = None if dh_out is None else _fit(dh_out, h.shape)
+        dh, dw = rmsnorm_residual_bwd_strided(dys, h, rstd, w, dres=dres,
+                                              deterministic=ctx.deterministic)
         dh = dh.view(ctx.shape)
         return dh, dh, dw, None, None
 

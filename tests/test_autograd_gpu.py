@@ -8,8 +8,10 @@ to both x and r), layernorm_fwd / layernorm_bwd. Checked with [..., H]
 inputs of more than two dimensions, an expanded (stride 0) incoming
 gradient, BF16 and FP32 weights (the BF16 weight's gradient is the FP32 dw
 rounded by autograd), an unused residual output, LayerNorm with and without
-beta, the modules, and repeated backward passes (deterministic dw). One
-case is also held to the oracle.
+beta, the modules, repeated backward passes (deterministic dw), per-head
+views of a wider buffer (plain and residual; passed to the strided entry
+points as they are) and a misaligned view (copied first). One case is also
+held to the oracle.
 """
 from __future__ import annotations
 
@@ -157,3 +159,77 @@ def test_modules():
     assert ln.weight.grad is not None and ln.bias.grad is not None
     assert ln.weight.grad.dtype == torch.bfloat16
     torch.cuda.synchronize()
+
+
+def test_rms_norm_head_views():
+    """Per-head views of a wider buffer go to the strided entry points as
+    they are; the gradient lands in the view's columns of the buffer only."""
+    T, heads, H, row = 2048, 24, 256, 8192
+    _announce(f"autograd rms_norm head views T={T} heads={heads} H={H} row={row}")
+    g = torch.Generator(device="cpu").manual_seed(9)
+    buf = torch.randn(T, row, generator=g).to(torch.bfloat16).to(DEV).requires_grad_()
+    w = (1 + 0.1 * torch.randn(H, generator=g)).to(DEV).requires_grad_()
+    dy = torch.randn(T, heads, H, generator=g).to(torch.bfloat16).to(DEV)
+    x = buf[:, : heads * H].view(T, heads, H)
+    assert not x.is_contiguous()
+    y = rn.rms_norm(x, w)
+    y.backward(dy)
+    torch.cuda.synchronize()
+    xd = buf.detach()[:, : heads * H].view(T, heads, H)
+    y_d, rstd = rn.rmsnorm_fwd_strided(xd, w.detach())
+    dx_d, dw_d = rn.rmsnorm_bwd_strided(dy, xd, rstd, w.detach())
+    torch.cuda.synchronize()
+    _same(y, y_d, "y")
+    _same(buf.grad[:, : heads * H].reshape(T, heads, H), dx_d, "dx")
+    assert not torch.any(buf.grad[:, heads * H:]), "gradient outside the view"
+    _same(w.grad, dw_d, "dw")
+
+
+def test_rms_norm_residual_head_views():
+    T, heads, H, row = 1024, 8, 256, 8192
+    _announce(f"autograd rms_norm_residual head views T={T} heads={heads} H={H}")
+    g = torch.Generator(device="cpu").manual_seed(10)
+    bx = torch.randn(T, row, generator=g).to(torch.bfloat16).to(DEV).requires_grad_()
+    br = torch.randn(T, row, generator=g).to(torch.bfloat16).to(DEV).requires_grad_()
+    w = (1 + 0.1 * torch.randn(H, generator=g)).to(torch.bfloat16).to(DEV).requires_grad_()
+    a = torch.randn(T, heads, H, generator=g).to(torch.bfloat16).to(DEV)
+    b = torch.randn(T, heads, H, generator=g).to(torch.bfloat16).to(DEV)
+    x = bx[:, : heads * H].view(T, heads, H)
+    r = br[:, 2048: 2048 + heads * H].view(T, heads, H)
+    y, h = rn.rms_norm_residual(x, r, w)
+    ((y.float() * a.float()).sum() + (h.float() * b.float()).sum()).backward()
+    torch.cuda.synchronize()
+    xd = bx.detach()[:, : heads * H].view(T, heads, H)
+    rd = br.detach()[:, 2048: 2048 + heads * H].view(T, heads, H)
+    h_d, y_d, rstd = rn.rmsnorm_residual_fwd_strided(xd, rd, w.detach())
+    dh_d, dw_d = rn.rmsnorm_residual_bwd_strided(a, h_d, rstd, w.detach(), dres=b)
+    torch.cuda.synchronize()
+    _same(y, y_d, "y")
+    _same(h, h_d, "h")
+    _same(bx.grad[:, : heads * H].reshape(T, heads, H), dh_d, "dx")
+    _same(br.grad[:, 2048: 2048 + heads * H].reshape(T, heads, H), dh_d, "dr")
+    _same(w.grad, dw_d.to(torch.bfloat16), "dw")
+
+
+def test_rms_norm_misaligned_view_is_copied():
+    """A view whose base is not 16-byte aligned is copied first: same bits
+    as the direct call on the contiguous copy."""
+    T, H = 777, 512
+    _announce(f"autograd rms_norm misaligned view T={T} H={H}")
+    g = torch.Generator(device="cpu").manual_seed(12)
+    buf = torch.randn(T, H + 4, generator=g).to(torch.bfloat16).to(DEV).requires_grad_()
+    w = (1 + 0.1 * torch.randn(H, generator=g)).to(DEV).requires_grad_()
+    dy = torch.randn(T, H, generator=g).to(torch.bfloat16).to(DEV)
+    x = buf[:, 4:]
+    assert x.data_ptr() % 16 != 0
+    y = rn.rms_norm(x, w)
+    y.backward(dy)
+    torch.cuda.synchronize()
+    xc = x.detach().contiguous()
+    y_d, rstd = rn.rmsnorm_fwd(xc, w.detach())
+    dx_d, dw_d = rn.rmsnorm_bwd(dy, xc, rstd, w.detach())
+    torch.cuda.synchronize()
+    _same(y, y_d, "y")
+    _same(buf.grad[:, 4:], dx_d, "dx")
+    assert not torch.any(buf.grad[:, :4])
+    _same(w.grad, dw_d, "dw")
