@@ -282,9 +282,12 @@ __device__ __forceinline__ void load_weights(const BwdParams& p, int slot, int l
 // Large-T row kernel: dx for the block's rows plus the block's dw sums.
 // Each iteration a row group takes U rows; with U <= 2 the next iteration's
 // rows are loaded before the current ones are processed.
+// Blocks of rows wider than a wave hold at most 512 threads once a lane
+// holds more than one 16-byte vector per tensor (NV * U >= 2): with 1024
+// the 128 registers a lane may use are too few and the tile spills.
 template <int NV, int U, typename WT, bool RES, bool WIDE, int MODE, bool RC = false, int NT = 0,
           bool CA = false>
-__global__ void __launch_bounds__(WIDE ? (NV * U >= 4 ? 512 : 1024) : 256) k_bwd_row(BwdParams p) {
+__global__ void __launch_bounds__(WIDE ? (NV * U >= 2 ? 512 : 1024) : 256) k_bwd_row(BwdParams p) {
     // Rows above 8192 elements take four vectors per lane on 512 lanes (a
     // 1024-lane group leaves 128 registers per lane); with the row unpacked
     // again after the exchange, the prefetched tile still fits (about 235
@@ -576,7 +579,8 @@ static int launch_row_t(const BwdParams& p, const Route& rt, hipStream_t s) {
     return launch_row_mode<NV, U, WT, RES, false, RC, CA>(p, rt, lds, s);
 }
 
-// (NV, U) pairs compiled: NV * U <= 8 with NV <= 2, and NV 4 with U 1.
+// (NV, U) pairs compiled: NV * U <= 4 (eight vectors per lane and tensor
+// spill at any block size).
 template <typename WT, bool RES, bool RC, bool CA>
 static int launch_row_shape(const BwdParams& p, const Route& rt, hipStream_t s) {
     const int nv = rt.r.vec_per_lane, u = rt.r.unroll;
@@ -586,13 +590,11 @@ static int launch_row_shape(const BwdParams& p, const Route& rt, hipStream_t s) 
             case 1: return launch_row_t<1, 1, WT, RES, RC, CA>(p, rt, s);
             case 2: return launch_row_t<1, 2, WT, RES, RC, CA>(p, rt, s);
             case 4: return launch_row_t<1, 4, WT, RES, RC, CA>(p, rt, s);
-            case 8: return launch_row_t<1, 8, WT, RES, RC, CA>(p, rt, s);
         }
     } else if (nv == 2) {
         switch (u) {
             case 1: return launch_row_t<2, 1, WT, RES, RC, CA>(p, rt, s);
             case 2: return launch_row_t<2, 2, WT, RES, RC, CA>(p, rt, s);
-            case 4: return launch_row_t<2, 4, WT, RES, RC, CA>(p, rt, s);
         }
     }
     return RMSN_ERR_SHAPE;

@@ -310,7 +310,7 @@ __device__ __forceinline__ void ln_row_sums2(float (&a)[U], float (&b)[U], int t
 }
 
 template <int NV, int U, typename WT, bool WIDE, bool F64, int NT>
-__global__ void __launch_bounds__(WIDE ? (NV * U >= 4 ? 512 : 1024) : 256)
+__global__ void __launch_bounds__(WIDE ? (NV * U >= 2 ? 512 : 1024) : 256)
     k_ln_bwd_row(LnBwdParams p) {
     // Rows of more than 8192 elements take 512 lanes with four vectors each
     // (a 1024-lane group would leave 128 registers per lane, too few for the

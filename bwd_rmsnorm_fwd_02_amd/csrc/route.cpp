@@ -196,8 +196,9 @@ Shape default_ln_bwd(int nvec) { return lookup(kLnBwdTable, nvec); }
 
 // Fill the row-kernel part of a route from a shape; 0 fields take defaults.
 // The checks mirror what the kernels are compiled for: (NV, U) pairs with
-// NV * U <= 8 (the backwards' NV 4 only with U = 1), blocks of <= 256
-// threads when a row fits in one wave, <= 512 when NV * U >= 4, else <= 1024.
+// NV * U <= 8 (the backwards' NV 4 only with U = 1, and NV * U <= 4 for the
+// RMSNorm backward), blocks of <= 256 threads when a row fits in one wave;
+// for wider rows <= 512 when NV * U >= 4 (the backwards: >= 2), else <= 1024.
 int row_shape(int op, int nvec, Shape sh, rmsn_route_t& r) {
     const int nv = sh.nv;
     // NV 4: the forwards (ops 0, 2), and the backwards (ops 1, 3) with U = 1
@@ -209,13 +210,15 @@ int row_shape(int op, int nvec, Shape sh, rmsn_route_t& r) {
     const int u = sh.unroll;
     if (!(u == 1 || u == 2 || u == 4 || u == 8)) return RMSN_ERR_SHAPE;
     if (nv * u > 8) return RMSN_ERR_SHAPE;
+    if (op == 1 && nv * u > 4) return RMSN_ERR_SHAPE;
     int rpb = sh.rpb;
     if (rpb <= 0) rpb = tpr <= 256 ? 256 / tpr : 1;
     if ((int64_t)rpb * tpr > 1024) return RMSN_ERR_SHAPE;
     const int threads = rpb * tpr;
     if (threads % 64 != 0) return RMSN_ERR_SHAPE;
     if (tpr <= 64 && threads > 256) return RMSN_ERR_SHAPE;
-    if (tpr > 64 && nv * u >= 4 && threads > 512) return RMSN_ERR_SHAPE;
+    const bool bwd = op == 1 || op == 3;
+    if (tpr > 64 && nv * u >= (bwd ? 2 : 4) && threads > 512) return RMSN_ERR_SHAPE;
     r.vec_per_lane = nv;
     r.lanes_per_row = tpr;
     r.rows_per_block = rpb;

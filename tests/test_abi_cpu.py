@@ -340,8 +340,20 @@ def test_route_override_selects_atomic_and_rejects_bad_knobs():
         assert st == 0 and r.vec_per_lane == 4 and r.lanes_per_row == 512
         assert lib.rmsnorm_route_override(1, ctypes.byref(K(2, 8, 0, 0, 0, 0))) == 0
         assert route(1, 4096, 4096, 0, 1)[0] == -3     # NV * U > 8 is not compiled
-        assert lib.rmsnorm_route_override(1, ctypes.byref(K(1, 8, 2, 0, 0, 0))) == 0
-        assert route(1, 4096, 4096, 0, 1)[0] == -3     # 1024 threads with NV * U >= 4
+        assert lib.rmsnorm_route_override(1, ctypes.byref(K(1, 8, 1, 0, 0, 0))) == 0
+        assert route(1, 4096, 4096, 0, 1)[0] == -3     # backward NV * U > 4 is not compiled
+        assert lib.rmsnorm_route_override(1, ctypes.byref(K(1, 2, 2, 0, 0, 0))) == 0
+        assert route(1, 4096, 4096, 0, 1)[0] == -3     # wide rows, NV * U >= 2: <= 512 threads
+        assert lib.rmsnorm_route_override(1, ctypes.byref(K(1, 2, 1, 0, 0, 0))) == 0
+        st, r = route(1, 4096, 4096, 0, 1)
+        assert st == 0 and r.block_threads == 512
+        assert lib.rmsnorm_route_override(3, ctypes.byref(K(2, 1, 8, 0, 0, 0))) == 0
+        assert route(3, 4096, 2048, 0, 1)[0] == -3     # LayerNorm backward: the same bound
+        assert lib.rmsnorm_route_override(3, ctypes.byref(K(2, 1, 4, 0, 0, 0))) == 0
+        st, r = route(3, 4096, 2048, 0, 1)
+        assert st == 0 and r.block_threads == 512
+        assert lib.rmsnorm_route_override(0, ctypes.byref(K(1, 8, 1, 0, 0, 0))) == 0
+        assert route(0, 4096, 4096)[0] == 0             # the forward keeps NV * U = 8
         assert lib.rmsnorm_route_override(1, ctypes.byref(K(2, 4, 0, 0, 0, 3))) == 0
         assert route(1, 4096, 4096, 0, 0)[0] == -3     # atomic variant compiled for NV 1, U <= 2
         assert lib.rmsnorm_route_override(1, ctypes.byref(K(1, 0, 64, 0, 0, 0))) == 0
@@ -355,6 +367,7 @@ def test_route_override_selects_atomic_and_rejects_bad_knobs():
     finally:
         lib.rmsnorm_route_override(0, None)
         lib.rmsnorm_route_override(1, None)
+        lib.rmsnorm_route_override(3, None)
     st, r = route(0, 4096, 256)
     assert st == 0 and (r.unroll, r.vec_per_lane, r.grid) == (before.unroll, before.vec_per_lane, before.grid)
 

@@ -356,7 +356,9 @@ VARIANTS = [
     (5000, 6144, "bf16", "bwd", dict(vec_per_lane=1, blocks_per_cu=2)),
     (777, 4096, "bf16", "fwd", dict(vec_per_lane=1, unroll=8)),
     (777, 6144, "bf16", "fwd", dict(vec_per_lane=2, unroll=4, rows_per_block=1)),
-    (777, 4096, "bf16", "bwd", dict(vec_per_lane=1, unroll=8, rows_per_block=1)),
+    (777, 4096, "bf16", "bwd", dict(vec_per_lane=1, unroll=4, rows_per_block=1)),
+    (777, 4096, "bf16", "bwd", dict(vec_per_lane=1, unroll=2, rows_per_block=1)),
+    (3000, 2048, "f32", "bwd", dict(vec_per_lane=2, unroll=1, rows_per_block=4)),
     (5000, 2048, "f32", "bwd", dict(vec_per_lane=1, unroll=4, rows_per_block=2)),
     (1000, 6144, "bf16", "bwd", dict(vec_per_lane=2, unroll=2)),
     (2500, 1024, "f32", "bwd", dict(kind=3)),  # atomic finalise, non-deterministic calls
