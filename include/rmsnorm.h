@@ -356,9 +356,12 @@ int rmsnorm_route_query(int op, int64_t rows, int64_t H, rmsn_dtype_t w_dtype,
  * not synchronised: set it while no other host thread is calling the
  * library. NULL clears. */
 typedef struct {
-    int vec_per_lane;   /* 1, 2 or 4 (backward 4 only with unroll 1) */
-    int unroll;         /* 1, 2 or 4; only 1 when a row spans several waves */
-    int rows_per_block; /* row groups per block; block size <= 1024 */
+    int vec_per_lane;   /* 1, 2 or 4 (the backwards: 4 only with unroll 1) */
+    int unroll;         /* 1, 2, 4 or 8, with vec_per_lane * unroll <= 8 (RMSNorm
+                           backward <= 4; LayerNorm backward: unroll <= 2) */
+    int rows_per_block; /* row groups per block. Block size <= 256 threads when a
+                           row fits in one wave, else <= 1024, and <= 512 once
+                           vec_per_lane * unroll >= 4 (the backwards: >= 2) */
     int blocks_per_cu;  /* grid cap = 256 * blocks_per_cu */
     int partial_f64;    /* backward: 1 FP64 partials, 2 FP32 partials */
     int kind;           /* backward: RMSN_KIND_BWD_ROW_DET or RMSN_KIND_BWD_ROW_ATOMIC */
